@@ -1,0 +1,288 @@
+"""CPU oracle for the block-scaled MoE expert GEMM path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+bench's ``cpu_baseline`` leg may import this package.  It shares no code with
+the HIP library (``block_scaled_precision_bsq_amd``) and never imports it.
+
+Bit-level codecs and quantizers live in ``bsq_oracle.c`` (plain C, IEEE binary32
+arithmetic, no FMA contraction); this module wraps them with numpy and adds the
+grouped GEMMs, which are written as "dequantize to float64, then multiply"
+(``numpy.matmul`` on float64 serves as the matmul step).
+
+Sources: "Composer 2 Technical Report" (papercache.org summary), section 6.1
+(NVFP4 variant in the MoE forward: E2M1 values, E4M3 scale per 16-element
+block, FP32 scale per token; standard MXFP8 in the backward: E4M3 values,
+E8M0 scale per 32; IEEE division for NVFP4 quantization) and "Cursor Composer 2
+report deep dive" (machinelearningatscale), section 1 "The kernel section".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bsq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+             "-fno-fast-math", "-fexcess-precision=standard", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (``force`` recompiles even if present)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I32 = ctypes.c_int32
+        U8 = ctypes.c_uint8
+        L.orc_e2m1_value.argtypes = [U8]; L.orc_e2m1_value.restype = ctypes.c_double
+        L.orc_e4m3_value.argtypes = [U8]; L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [U8]; L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_e2m1_encode.argtypes = [ctypes.c_float]; L.orc_e2m1_encode.restype = U8
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]; L.orc_e4m3_encode.restype = U8
+        L.orc_e2m1_encode_array.argtypes = [P, P, I64]; L.orc_e2m1_encode_array.restype = None
+        L.orc_e4m3_encode_array.argtypes = [P, P, I64]; L.orc_e4m3_encode_array.restype = None
+        L.orc_quantize_nvfp4v.argtypes = [P, I64, I64, I64, P, P, P]; L.orc_quantize_nvfp4v.restype = None
+        L.orc_dequant_nvfp4v.argtypes = [P, P, P, I64, I64, P]; L.orc_dequant_nvfp4v.restype = None
+        L.orc_quantize_mxfp8_rowwise.argtypes = [P, I64, I64, I64, P, P]
+        L.orc_quantize_mxfp8_rowwise.restype = None
+        L.orc_colwise_padded_cols.argtypes = [I32, I64]; L.orc_colwise_padded_cols.restype = I64
+        L.orc_quantize_mxfp8_colwise_t.argtypes = [P, I64, I64, I64, P, I32, P, P]
+        L.orc_quantize_mxfp8_colwise_t.restype = None
+        L.orc_dequant_mxfp8.argtypes = [P, P, I64, I64, I64, I64, P]; L.orc_dequant_mxfp8.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _bf16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("oracle inputs are bf16 bit patterns (uint16)")
+    return x
+
+
+# ------------------------------------------------------------------ codecs
+
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(code)
+
+
+def e4m3_value(b: int) -> float:
+    return lib().orc_e4m3_value(b)
+
+
+def e8m0_value(b: int) -> float:
+    return lib().orc_e8m0_value(b)
+
+
+def e2m1_encode(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().orc_e2m1_encode_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def e4m3_encode(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint8)
+    lib().orc_e4m3_encode_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+E2M1_TABLE = None
+E4M3_TABLE = None
+E8M0_TABLE = None
+
+
+def tables():
+    """Decode tables (float64) for all 16 E2M1, 256 E4M3 and 256 E8M0 codes."""
+    global E2M1_TABLE, E4M3_TABLE, E8M0_TABLE
+    if E2M1_TABLE is None:
+        E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)])
+        E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)])
+        E8M0_TABLE = np.array([e8m0_value(c) for c in range(256)])
+    return E2M1_TABLE, E4M3_TABLE, E8M0_TABLE
+
+
+# -------------------------------------------------------------- quantizers
+
+def quantize_nvfp4v(x_bf16: np.ndarray):
+    """NVFP4 variant of each row of a [rows, cols] bf16 matrix.
+
+    Returns (codes [rows, cols/2] u8, bscale [rows, cols/16] u8 (E4M3),
+    rscale [rows] f32 (decode scale)).
+    """
+    x = _bf16(x_bf16)
+    rows, cols = x.shape
+    if cols % 16:
+        raise ValueError("cols must be a multiple of 16")
+    codes = np.empty((rows, cols // 2), np.uint8)
+    bscale = np.empty((rows, cols // 16), np.uint8)
+    rscale = np.empty((rows,), np.float32)
+    lib().orc_quantize_nvfp4v(_ptr(x), rows, cols, cols, _ptr(codes), _ptr(bscale), _ptr(rscale))
+    return codes, bscale, rscale
+
+
+def dequant_nvfp4v(codes, bscale, rscale) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    bscale = np.ascontiguousarray(bscale, np.uint8)
+    rscale = np.ascontiguousarray(rscale, np.float32)
+    rows, half = codes.shape
+    out = np.empty((rows, 2 * half), np.float64)
+    lib().orc_dequant_nvfp4v(_ptr(codes), _ptr(bscale), _ptr(rscale), rows, 2 * half, _ptr(out))
+    return out
+
+
+def quantize_mxfp8_rowwise(x_bf16: np.ndarray):
+    """MXFP8 with blocks of 32 along each row.  Returns (codes [rows, cols],
+    scale [rows, cols/32])."""
+    x = _bf16(x_bf16)
+    rows, cols = x.shape
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    codes = np.empty((rows, cols), np.uint8)
+    scale = np.empty((rows, cols // 32), np.uint8)
+    lib().orc_quantize_mxfp8_rowwise(_ptr(x), rows, cols, cols, _ptr(codes), _ptr(scale))
+    return codes, scale
+
+
+def padded_cols(ngroups: int, rows: int) -> int:
+    return int(lib().orc_colwise_padded_cols(ngroups, rows))
+
+
+def segment_start(g: int, offsets) -> int:
+    """First padded column of segment g in the COLWISE_T layout."""
+    return 32 * (g + int(offsets[g]) // 32)
+
+
+def quantize_mxfp8_colwise_t(x_bf16: np.ndarray, offsets):
+    """MXFP8 with blocks of 32 running down the rows of each segment
+    ``[offsets[g], offsets[g+1])``; output transposed and per-segment padded.
+    Returns (codes [cols, P], scale [cols, P/32])."""
+    x = _bf16(x_bf16)
+    rows, cols = x.shape
+    off = np.ascontiguousarray(offsets, np.int32)
+    G = len(off) - 1
+    P = padded_cols(G, rows)
+    codes = np.empty((cols, P), np.uint8)
+    scale = np.empty((cols, P // 32), np.uint8)
+    lib().orc_quantize_mxfp8_colwise_t(_ptr(x), rows, cols, cols, _ptr(off), G, _ptr(codes), _ptr(scale))
+    return codes, scale
+
+
+def dequant_mxfp8(codes, scale) -> np.ndarray:
+    """Dequantize a matrix whose MXFP8 blocks run along its rows (ROWWISE
+    output, or a COLWISE_T output read as [cols, P])."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scale = np.ascontiguousarray(scale, np.uint8)
+    rows, cols = codes.shape
+    out = np.empty((rows, cols), np.float64)
+    lib().orc_dequant_mxfp8(_ptr(codes), _ptr(scale), rows, cols, cols, scale.shape[1], _ptr(out))
+    return out
+
+
+# ------------------------------------------------------------ grouped GEMMs
+
+def _expert_of_rows(offsets, rows):
+    off = np.asarray(offsets, np.int64)
+    return np.searchsorted(off, rows, side="right") - 1
+
+
+def grouped_gemm_fwd(a_q, w_q, offsets, rows=None) -> np.ndarray:
+    """Forward expert GEMM over NVFP4-variant operands, in float64.
+
+    ``a_q`` = (codes [M, K/2], bscale [M, K/16], rscale [M]) for the
+    expert-sorted activations; ``w_q`` = the same for the weights stacked as
+    [E*N, ...] (expert e owns rows e*N .. e*N+N-1).  Returns
+    Y[m, n] = sum_k A_hat[m, k] * W_hat_e[n, k] for m in segment e, over all m
+    (or only the listed ``rows``, in that order).
+    """
+    off = np.asarray(offsets, np.int64)
+    E = len(off) - 1
+    M = a_q[0].shape[0]
+    N = w_q[0].shape[0] // E
+    rows = np.arange(M) if rows is None else np.asarray(rows, np.int64)
+    exp_of = _expert_of_rows(off, rows)
+    y = np.zeros((len(rows), N), np.float64)
+    for e in np.unique(exp_of):
+        sel = np.nonzero(exp_of == e)[0]
+        r = rows[sel]
+        a_hat = dequant_nvfp4v(a_q[0][r], a_q[1][r], a_q[2][r])
+        sl = slice(e * N, (e + 1) * N)
+        w_hat = dequant_nvfp4v(w_q[0][sl], w_q[1][sl], w_q[2][sl])
+        y[sel] = a_hat @ w_hat.T
+    return y
+
+
+def grouped_gemm_dgrad(dy_q, wt_q, offsets, n, rows=None) -> np.ndarray:
+    """dX[m, k] = sum_n dY_hat[m, n] * W_hat_e[n, k] (float64).
+
+    ``dy_q`` = ROWWISE MXFP8 of dY [M, N]; ``wt_q`` = COLWISE_T MXFP8 of the
+    weights [E*N, K] with segments of N rows per expert, i.e. codes [K, P_w].
+    """
+    off = np.asarray(offsets, np.int64)
+    E = len(off) - 1
+    M = dy_q[0].shape[0]
+    K = wt_q[0].shape[0]
+    rows = np.arange(M) if rows is None else np.asarray(rows, np.int64)
+    exp_of = _expert_of_rows(off, rows)
+    woff = np.arange(E + 1, dtype=np.int64) * n
+    out = np.zeros((len(rows), K), np.float64)
+    for e in np.unique(exp_of):
+        sel = np.nonzero(exp_of == e)[0]
+        r = rows[sel]
+        dy_hat = dequant_mxfp8(dy_q[0][r], dy_q[1][r])
+        c0 = segment_start(int(e), woff)
+        wt_hat = dequant_mxfp8(wt_q[0][:, c0:c0 + n], wt_q[1][:, c0 // 32:c0 // 32 + n // 32])
+        out[sel] = dy_hat @ wt_hat.T
+    return out
+
+
+def grouped_gemm_wgrad(dyt_q, xt_q, offsets, experts=None) -> dict:
+    """dW_e[n, k] = sum_{m in segment e} dY_hat[m, n] * X_hat[m, k] (float64).
+
+    ``dyt_q`` / ``xt_q`` = COLWISE_T MXFP8 of dY [M, N] and X [M, K] with the
+    expert offsets.  Returns {e: dW_e [N, K]} for the listed (default: all)
+    experts; an empty expert gives zeros.
+    """
+    off = np.asarray(offsets, np.int64)
+    E = len(off) - 1
+    experts = range(E) if experts is None else experts
+    res = {}
+    for e in experts:
+        m_e = int(off[e + 1] - off[e])
+        c0 = segment_start(int(e), off)
+        L = 32 * ((m_e + 31) // 32)
+        dyt = dequant_mxfp8(dyt_q[0][:, c0:c0 + L], dyt_q[1][:, c0 // 32:c0 // 32 + L // 32])
+        xt = dequant_mxfp8(xt_q[0][:, c0:c0 + L], xt_q[1][:, c0 // 32:c0 // 32 + L // 32])
+        res[int(e)] = dyt @ xt.T
+    return res
+
+
+def swiglu(gu: np.ndarray) -> np.ndarray:
+    """Harness activation between the two forward GEMMs (not on the pages):
+    [gate | up] along the last axis, H = silu(gate) * up, in float64."""
+    g, u = np.split(np.asarray(gu, np.float64), 2, axis=-1)
+    return g / (1.0 + np.exp(-g)) * u
