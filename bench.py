@@ -1,0 +1,267 @@
+"""Benchmark of the block-scaled MoE expert grouped GEMM path on one MI355X.
+
+One step = the whole hot path over one batch of the 32-expert shard
+(hidden 7168, intermediate 2048, 32768 routed token-slots, Zipf(1.1) expert
+popularity), inputs resident in HBM:
+  forward  : NVFP4-variant quantize of W_gu, W_down (once per weight version,
+             i.e. every optimizer step) and of X; gate/up grouped GEMM;
+             SwiGLU (harness, torch); quantize H; down grouped GEMM;
+  backward : MXFP8 quantize of dY (row-wise and per-expert transposed), of the
+             weights (transposed) and of H, dGU, X (transposed); dgrad and
+             wgrad grouped GEMMs of the down and the gate/up projections.
+dGU is synthetic N(0, 1e-3) (the backward workload's own input).
+
+Prints ONE JSON line: metric/value = grouped-GEMM TFLOP/s of the whole step
+(all six GEMMs' algorithmic flops / step time), per-stage breakdown (HIP-event
+times on the stream the kernels run on), the roofline of the dominant kernel
+and the CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --mode copy      # plain device copy (counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"f16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}  # dense MFMA TFLOP/s (MI355X)
+HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["step", "copy"], default="step")
+    return ap.parse_args()
+
+
+def copy_mode():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is built and measured "
+              f"for a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy":
+        copy_mode()
+        return
+    import numpy as np
+    import torch
+
+    from block_scaled_precision_bsq_amd.build import LIB
+    if not os.path.exists(LIB):
+        from block_scaled_precision_bsq_amd.build import build
+        build()
+    import block_scaled_precision_bsq_amd as bsq
+    from workloads import CONFIGS, moe_counts, offsets_from_counts
+
+    cfg = CONFIGS[3]
+    E, Hd, I, M = cfg.n_experts, cfg.hidden, cfg.inter, cfg.m_total
+    counts = moe_counts(cfg)
+    off_np = offsets_from_counts(counts)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev).manual_seed(20250)
+    bf = torch.bfloat16
+
+    def randn(shape, sigma=1.0):
+        return (torch.randn(shape, generator=gen, device=dev) * sigma).to(bf)
+
+    x = randn((M, Hd))
+    w_gu = randn((E * 2 * I, Hd), 0.02)       # [E][2I][H]: gate rows then up rows
+    w_dn = randn((E * Hd, I), 0.02)           # [E][H][I]
+    dy = randn((M, Hd), 1e-3)
+    dgu = randn((M, 2 * I), 1e-3)
+    off = torch.from_numpy(off_np).to(dev)
+    woff_gu = torch.arange(E + 1, dtype=torch.int32, device=dev) * (2 * I)
+    woff_dn = torch.arange(E + 1, dtype=torch.int32, device=dev) * Hd
+    ws_f = torch.empty(bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_FWD, E, M, 8192, 8192), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_BWD, E, M, 8192, 8192), dtype=torch.uint8, device=dev)
+
+    # preallocated outputs (the step allocates nothing)
+    def nv(rows, cols):
+        return (torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
+                torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
+                torch.empty((rows,), dtype=torch.float32, device=dev))
+
+    def mxr(rows, cols):
+        return (torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev))
+
+    def mxc(rows, cols, groups):
+        P = bsq.bsq_colwise_padded_cols(groups, rows)
+        return (torch.empty((cols, P), dtype=torch.uint8, device=dev),
+                torch.empty((cols, P // 32), dtype=torch.uint8, device=dev))
+
+    q_wgu, q_wdn, q_x, q_h = nv(E * 2 * I, Hd), nv(E * Hd, I), nv(M, Hd), nv(M, I)
+    gu = torch.empty((M, 2 * I), dtype=bf, device=dev)
+    h = torch.empty((M, I), dtype=bf, device=dev)
+    y = torch.empty((M, Hd), dtype=bf, device=dev)
+    q_dy, q_dgu = mxr(M, Hd), mxr(M, 2 * I)
+    t_wdn, t_wgu = mxc(E * Hd, I, E), mxc(E * 2 * I, Hd, E)
+    t_dy, t_h, t_dgu, t_x = mxc(M, Hd, E), mxc(M, I, E), mxc(M, 2 * I, E), mxc(M, Hd, E)
+    dh = torch.empty((M, I), dtype=bf, device=dev)
+    dx = torch.empty((M, Hd), dtype=bf, device=dev)
+    dw_dn = torch.empty((E, Hd, I), dtype=bf, device=dev)
+    dw_gu = torch.empty((E, 2 * I, Hd), dtype=bf, device=dev)
+
+    R, C = bsq.BSQ_ROWWISE, bsq.BSQ_COLWISE_T
+    stages = [
+        ("quant_nvfp4v_weights", lambda: (bsq.bsq_quantize_nvfp4v(w_gu, *q_wgu), bsq.bsq_quantize_nvfp4v(w_dn, *q_wdn))),
+        ("quant_nvfp4v_x", lambda: bsq.bsq_quantize_nvfp4v(x, *q_x)),
+        ("gemm_fwd_gate_up", lambda: bsq.bsq_grouped_gemm_fwd(q_x, q_wgu, off, 2 * I, Hd, y=gu, workspace=ws_f)),
+        ("swiglu", None),
+        ("quant_nvfp4v_h", lambda: bsq.bsq_quantize_nvfp4v(h, *q_h)),
+        ("gemm_fwd_down", lambda: bsq.bsq_grouped_gemm_fwd(q_h, q_wdn, off, Hd, I, y=y, workspace=ws_f)),
+        ("quant_mxfp8_rowwise", lambda: (bsq.bsq_quantize_mxfp8(dy, R, codes=q_dy[0], scale=q_dy[1]),
+                                         bsq.bsq_quantize_mxfp8(dgu, R, codes=q_dgu[0], scale=q_dgu[1]))),
+        ("quant_mxfp8_colwise_t", lambda: (
+            bsq.bsq_quantize_mxfp8(w_dn, C, offsets=woff_dn, codes=t_wdn[0], scale=t_wdn[1]),
+            bsq.bsq_quantize_mxfp8(w_gu, C, offsets=woff_gu, codes=t_wgu[0], scale=t_wgu[1]),
+            bsq.bsq_quantize_mxfp8(dy, C, offsets=off, codes=t_dy[0], scale=t_dy[1]),
+            bsq.bsq_quantize_mxfp8(h, C, offsets=off, codes=t_h[0], scale=t_h[1]),
+            bsq.bsq_quantize_mxfp8(dgu, C, offsets=off, codes=t_dgu[0], scale=t_dgu[1]),
+            bsq.bsq_quantize_mxfp8(x, C, offsets=off, codes=t_x[0], scale=t_x[1]))),
+        ("gemm_bwd_dgrad_down", lambda: bsq.bsq_grouped_gemm_bwd(off, M, Hd, I, dy_q=q_dy, wt_q=t_wdn,
+                                                                 flags=bsq.BSQ_DGRAD, dx=dh, workspace=ws_b)),
+        ("gemm_bwd_wgrad_down", lambda: bsq.bsq_grouped_gemm_bwd(off, M, Hd, I, dyt_q=t_dy, xt_q=t_h,
+                                                                 flags=bsq.BSQ_WGRAD, dw=dw_dn, workspace=ws_b)),
+        ("gemm_bwd_dgrad_gate_up", lambda: bsq.bsq_grouped_gemm_bwd(off, M, 2 * I, Hd, dy_q=q_dgu, wt_q=t_wgu,
+                                                                    flags=bsq.BSQ_DGRAD, dx=dx, workspace=ws_b)),
+        ("gemm_bwd_wgrad_gate_up", lambda: bsq.bsq_grouped_gemm_bwd(off, M, 2 * I, Hd, dyt_q=t_dgu, xt_q=t_x,
+                                                                    flags=bsq.BSQ_WGRAD, dw=dw_gu, workspace=ws_b)),
+    ]
+
+    def swiglu_into():  # harness activation between the GEMMs: H = silu(gate) * up
+        h.copy_(torch.nn.functional.silu(gu[:, :I].float()).mul_(gu[:, I:].float()))
+    stages[3] = ("swiglu", swiglu_into)
+
+    flops = {
+        "gemm_fwd_gate_up": 2.0 * M * 2 * I * Hd, "gemm_fwd_down": 2.0 * M * Hd * I,
+        "gemm_bwd_dgrad_down": 2.0 * M * Hd * I, "gemm_bwd_wgrad_down": 2.0 * M * Hd * I,
+        "gemm_bwd_dgrad_gate_up": 2.0 * M * 2 * I * Hd, "gemm_bwd_wgrad_gate_up": 2.0 * M * 2 * I * Hd,
+    }
+    nvb = lambda r, c: 2 * r * c + r * c // 2 + r * c // 16 + 4 * r           # bf16 in + codes + scales + rscale
+    mxb = lambda r, c: 2 * r * c + r * c + r * c // 32                       # bf16 in + codes + scales
+    qbytes = {
+        "quant_nvfp4v_weights": nvb(E * 2 * I, Hd) + nvb(E * Hd, I), "quant_nvfp4v_x": nvb(M, Hd),
+        "quant_nvfp4v_h": nvb(M, I), "quant_mxfp8_rowwise": mxb(M, Hd) + mxb(M, 2 * I),
+        "quant_mxfp8_colwise_t": mxb(E * Hd, I) + mxb(E * 2 * I, Hd) + mxb(M, Hd) + mxb(M, I) + mxb(M, 2 * I)
+        + mxb(M, Hd),
+    }
+
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(stages):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = {nm: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+                for i, (nm, _) in enumerate(stages)}
+    total_flops = sum(flops.values())
+    breakdown = {}
+    for nm, ms in stage_ms.items():
+        d = {"ms": round(ms, 4)}
+        if nm in flops:
+            tf = flops[nm] / (ms * 1e-3) / 1e12
+            peak = PEAK["f16"] if "fwd" in nm else PEAK["fp8"]
+            d.update({"tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / peak, 4),
+                      "mfma": "f16 (exact E2M1xE4M3 dequant)" if "fwd" in nm else "fp8 e4m3 block-scaled"})
+        if nm in qbytes:
+            gbs = qbytes[nm] / (ms * 1e-3) / 1e9
+            d.update({"gbps": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_GBS, 4)})
+        breakdown[nm] = d
+    dom = max(flops, key=lambda k: stage_ms[k])
+    dom_tf = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    dom_peak = PEAK["f16"] if "fwd" in dom else PEAK["fp8"]
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 1), "peak": dom_peak,
+                "unit": "TFLOP/s", "frac": round(dom_tf / dom_peak, 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, counts, off_np)
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "grouped-GEMM TFLOP/s (% of MFMA peak) + quantize GB/s, 32 experts 7168x2048",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fwd: E2M1xE4M3 dequantized exactly to f16, f16 MFMA; bwd: E4M3 block-scaled MFMA; fp32 accumulate",
+        "data": "synthetic (seeded torch.randn; Zipf(1.1) expert counts)",
+        "config": {"workload": "MoE expert shard fwd+bwd: 32 experts, hidden 7168, intermediate 2048, "
+                               "32768 routed token-slots, Zipf(1.1); NVFP4-variant fwd, MXFP8 bwd",
+                   "experts": E, "hidden": Hd, "intermediate": I, "token_slots": M,
+                   "gemm_tflop_per_step": round(total_flops / 1e12, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(cfg, counts, off_np):
+    """The oracle as it stands, on a bounded sample: NVFP4-variant quantize +
+    float64 forward gate/up GEMM for the first rows of a few experts."""
+    import numpy as np
+
+    import oracle
+    from workloads import normal_bf16, rng_for
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = os.cpu_count() or 1
+    rng = rng_for(3, salt=55)
+    Hd, I = cfg.hidden, cfg.inter
+    sample_experts = [int(e) for e in np.argsort(-np.asarray(counts))[:4]]
+    rows_per = 2048
+    inputs = [(normal_bf16(rng, (min(rows_per, int(counts[e])), Hd)), normal_bf16(rng, (2 * I, Hd), 0.02))
+              for e in sample_experts]
+    flops = 0.0
+    t0 = time.perf_counter()
+    for x, w in inputs:
+        a_q, w_q = oracle.quantize_nvfp4v(x), oracle.quantize_nvfp4v(w)
+        oracle.grouped_gemm_fwd(a_q, w_q, np.array([0, x.shape[0]], np.int32))
+        flops += 2.0 * x.shape[0] * 2 * I * Hd
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"NVFP4-variant quantize + float64 gate/up GEMM of the first {rows_per} token-slots of the "
+                      f"{len(sample_experts)} largest experts (n=4096, k=7168); seconds={dt:.1f}"}
+
+
+if __name__ == "__main__":
+    main()

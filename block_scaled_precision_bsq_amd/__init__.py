@@ -1,0 +1,230 @@
+"""Python binding of libbsq.so: block-scaled MoE expert grouped GEMM on MI355X.
+
+Thin ctypes marshalling over the C ABI declared in ``include/bsq.h``: every
+function here has the C entry point's name, checks tensor dtypes, shapes and
+devices, passes raw device pointers plus torch's current HIP stream, and turns
+a non-OK status into ``RuntimeError``.  All arithmetic runs in the HIP kernels;
+torch only provides device memory and streams.  There is no CPU fallback:
+importing this package fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_scaled_precision_bsq_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+I32 = ctypes.c_int32
+INT = ctypes.c_int
+
+BSQ_OK, BSQ_ERR_INVALID_ARG, BSQ_ERR_UNSUPPORTED, BSQ_ERR_WORKSPACE_TOO_SMALL, BSQ_ERR_HIP = range(5)
+BSQ_BF16, BSQ_F32 = 0, 1
+BSQ_ROWWISE, BSQ_COLWISE_T = 0, 1
+BSQ_DGRAD, BSQ_WGRAD = 1, 2
+BSQ_OP_GEMM_FWD, BSQ_OP_GEMM_BWD = 0, 1
+
+_SIGS = {
+    "bsq_quantize_nvfp4v": ([P, I64, I64, I64, P, I32, P, P, P, P], INT),
+    "bsq_quantize_mxfp8": ([P, I64, I64, I64, INT, P, I32, P, P, P], INT),
+    "bsq_grouped_gemm_fwd": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
+    "bsq_grouped_gemm_bwd": ([P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, INT, ctypes.c_uint, P,
+                              ctypes.c_size_t, P], INT),
+    "bsq_workspace_size": ([INT, I32, I64, I64, I64], ctypes.c_size_t),
+    "bsq_colwise_padded_cols": ([I32, I64], I64),
+    "bsq_status_string": ([INT], ctypes.c_char_p),
+    "bsq_abi_version": ([], INT),
+    "bsq_debug_status": ([P, P, ctypes.POINTER(I32)], INT),
+    "bsq_debug_encode_e2m1": ([P, P, I64, P], INT),
+    "bsq_debug_encode_e4m3": ([P, P, I64, P], INT),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+ABI_VERSION = _lib.bsq_abi_version()
+
+
+class BsqError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {_lib.bsq_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != BSQ_OK:
+        raise BsqError(fn, status)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t, name, dtypes):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _rows_ld(x):
+    if x.dim() != 2:
+        raise ValueError("x must be a 2-D matrix")
+    rows, cols = x.shape
+    if rows == 0 or cols == 0:
+        return rows, cols, cols
+    if x.stride(1) != 1 and cols > 1:
+        raise ValueError("x must be row-major (unit column stride)")
+    return rows, cols, x.stride(0) if rows > 1 else cols
+
+
+def bsq_workspace_size(op, num_experts, m_total, n, k):
+    return int(_lib.bsq_workspace_size(op, num_experts, m_total, n, k))
+
+
+def bsq_colwise_padded_cols(num_groups, rows):
+    return int(_lib.bsq_colwise_padded_cols(num_groups, rows))
+
+
+def bsq_quantize_nvfp4v(x, codes=None, bscale=None, rscale=None, offsets=None, stream=None):
+    """NVFP4-variant quantization of each row of bf16 ``x`` [rows, cols].
+    Returns (codes u8 [rows, cols/2], bscale u8 [rows, cols/16], rscale f32 [rows])."""
+    _dev(x, "x", _BF16)
+    rows, cols, ld = _rows_ld(x)
+    dev = x.device
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    bscale = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev) if bscale is None else bscale
+    rscale = torch.empty((rows,), dtype=torch.float32, device=dev) if rscale is None else rscale
+    for t, nm, shape in ((codes, "codes", (rows, cols // 2)), (bscale, "bscale", (rows, cols // 16)),
+                         (rscale, "rscale", (rows,))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous with shape {shape}")
+    ng = 0 if offsets is None else offsets.numel() - 1
+    _check("bsq_quantize_nvfp4v",
+           _lib.bsq_quantize_nvfp4v(_ptr(x), rows, cols, ld, _ptr(offsets), ng, _ptr(codes), _ptr(bscale),
+                                    _ptr(rscale), _stream(stream)))
+    return codes, bscale, rscale
+
+
+def bsq_quantize_mxfp8(x, axis=BSQ_ROWWISE, offsets=None, codes=None, scale=None, stream=None):
+    """MXFP8 quantization of bf16 ``x`` [rows, cols].
+    ROWWISE: (codes [rows, cols], scale [rows, cols/32]).
+    COLWISE_T (needs int32 device ``offsets``): (codes [cols, P], scale [cols, P/32])."""
+    _dev(x, "x", _BF16)
+    rows, cols, ld = _rows_ld(x)
+    dev = x.device
+    if axis == BSQ_ROWWISE:
+        shapes = ((rows, cols), (rows, cols // 32))
+        ng = 0
+    else:
+        if offsets is None:
+            raise ValueError("COLWISE_T needs offsets")
+        _dev(offsets, "offsets", (torch.int32,))
+        ng = offsets.numel() - 1
+        Pc = bsq_colwise_padded_cols(ng, rows)
+        shapes = ((cols, Pc), (cols, Pc // 32))
+    codes = torch.empty(shapes[0], dtype=torch.uint8, device=dev) if codes is None else codes
+    scale = torch.empty(shapes[1], dtype=torch.uint8, device=dev) if scale is None else scale
+    for t, nm, shape in ((codes, "codes", shapes[0]), (scale, "scale", shapes[1])):
+        if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous with shape {shape}")
+    _check("bsq_quantize_mxfp8",
+           _lib.bsq_quantize_mxfp8(_ptr(x), rows, cols, ld, axis, _ptr(offsets), ng, _ptr(codes), _ptr(scale),
+                                   _stream(stream)))
+    return codes, scale
+
+
+def _workspace(op, E, m_total, n, k, workspace, dev):
+    need = bsq_workspace_size(op, E, m_total, n, k)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    return workspace
+
+
+def bsq_grouped_gemm_fwd(a_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, workspace=None, stream=None):
+    """Forward grouped GEMM.  a_q / w_q = (codes, bscale, rscale) of the
+    expert-sorted activations [m_total, k] and of the weights [E*n, k]."""
+    a_codes, a_bscale, a_rscale = a_q
+    w_codes, w_bscale, w_rscale = w_q
+    _dev(offsets, "offsets", (torch.int32,))
+    E = offsets.numel() - 1
+    m_total = a_codes.shape[0]
+    if w_codes.shape[0] != E * n:
+        raise ValueError("weights must hold num_experts * n rows")
+    dev = a_codes.device
+    if y is None:
+        y = torch.empty((m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev)
+    _check("bsq_grouped_gemm_fwd",
+           _lib.bsq_grouped_gemm_fwd(_ptr(a_codes), _ptr(a_bscale), _ptr(a_rscale), _ptr(w_codes), _ptr(w_bscale),
+                                     _ptr(w_rscale), _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+    return y
+
+
+def bsq_grouped_gemm_bwd(offsets, m_total, n, k, dy_q=None, wt_q=None, dyt_q=None, xt_q=None,
+                         flags=BSQ_DGRAD | BSQ_WGRAD, dx_dtype=BSQ_BF16, dw_dtype=BSQ_BF16, dx=None, dw=None,
+                         workspace=None, stream=None):
+    """Backward grouped GEMMs.  dy_q = ROWWISE (codes, scale) of dY [m_total, n];
+    wt_q = COLWISE_T of W [E*n, k] with offsets {0, n, 2n, ..}; dyt_q / xt_q =
+    COLWISE_T of dY / X with ``offsets``.  Returns (dx, dw)."""
+    _dev(offsets, "offsets", (torch.int32,))
+    E = offsets.numel() - 1
+    dev = offsets.device
+    if flags & BSQ_DGRAD and dx is None and m_total > 0:
+        dx = torch.empty((m_total, k), dtype=torch.float32 if dx_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    if flags & BSQ_WGRAD and dw is None:
+        dw = torch.empty((E, n, k), dtype=torch.float32 if dw_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_BWD, E, m_total, n, k, workspace, dev)
+    dy_q = dy_q or (None, None)
+    wt_q = wt_q or (None, None)
+    dyt_q = dyt_q or (None, None)
+    xt_q = xt_q or (None, None)
+    _check("bsq_grouped_gemm_bwd",
+           _lib.bsq_grouped_gemm_bwd(_ptr(dy_q[0]), _ptr(dy_q[1]), _ptr(wt_q[0]), _ptr(wt_q[1]), _ptr(dyt_q[0]),
+                                     _ptr(dyt_q[1]), _ptr(xt_q[0]), _ptr(xt_q[1]), _ptr(offsets), E, m_total, n, k,
+                                     _ptr(dx), dx_dtype, _ptr(dw), dw_dtype, flags, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dx, dw
+
+
+def bsq_debug_status(workspace, stream=None):
+    v = I32(0)
+    _check("bsq_debug_status", _lib.bsq_debug_status(_ptr(workspace), _stream(stream), ctypes.byref(v)))
+    return int(v.value)
+
+
+def bsq_debug_encode_e2m1(x, out=None, stream=None):
+    _dev(x, "x", (torch.float32,))
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    _check("bsq_debug_encode_e2m1", _lib.bsq_debug_encode_e2m1(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out
+
+
+def bsq_debug_encode_e4m3(x, out=None, stream=None):
+    _dev(x, "x", (torch.float32,))
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    _check("bsq_debug_encode_e4m3", _lib.bsq_debug_encode_e4m3(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out

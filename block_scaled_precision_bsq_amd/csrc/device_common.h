@@ -1,0 +1,123 @@
+// Device helpers shared by the gfx950 kernels of libbsq.
+//
+// Number formats (named in "Composer 2 Technical Report", section 6.1):
+//  E2M1  sign + 2-bit exponent (bias 1) + 1-bit mantissa, magnitudes
+//        0, .5, 1, 1.5, 2, 3, 4, 6.
+//  E4M3  OCP E4M3FN, bias 7, subnormals m * 2^-9, max 448.
+//  E8M0  2^(byte - 127).
+// All encoders round to nearest even and saturate (E2M1 at 6, E4M3 at 448).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef int int8v __attribute__((ext_vector_type(8)));
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (data read once: nontemporal hint).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// |bf16| maximum of the two halves of w and of m (bit patterns; valid for
+// non-NaN values because magnitudes order like their bit patterns).
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t m, uint32_t w) {
+    uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+    return max(m, max(lo, hi));
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E2M1 codes of two floats into nibbles of byte `sel` of `old`: low nibble
+// from a, high nibble from b.  The hardware conversion rounds to nearest
+// even, saturates to +-6 and keeps the sign of zero; a unit scale leaves the
+// values unchanged (checked exhaustively against the CPU oracle).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2(uint32_t old, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// E4M3 bytes of four floats (any non-NaN values), a in the lowest byte:
+// clamp to +-448 first, the hardware conversion then rounds to nearest even
+// (checked exhaustively against the CPU oracle).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, 448.0f, -448.0f);
+    b = __builtin_amdgcn_fmed3f(b, 448.0f, -448.0f);
+    c = __builtin_amdgcn_fmed3f(c, 448.0f, -448.0f);
+    d = __builtin_amdgcn_fmed3f(d, 448.0f, -448.0f);
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+// Exact value of an E4M3 byte with clear sign bit (0..0x7E).
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    float sub = (float)m * 0x1p-9f;
+    return e ? normal : sub;
+}
+
+// Wave-wide maximum (wave64) of a non-negative value's bit pattern.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+}  // namespace bsq
+
+namespace bsq {
+
+// Raw buffer resource over [base, base + bytes): loads through it take a
+// 32-bit byte offset and return zero when the access lies beyond `bytes`
+// (used for row and k masking).  bytes must stay below 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // offset that always reads zero
+
+// Mark a wave-uniform value as such (keeps it, and what is derived from it,
+// in SGPRs; buffer resources built from divergent-looking values otherwise
+// force a readfirstlane loop around every load).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_bit_cast(uint8_t, __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0));
+}
+
+}  // namespace bsq

@@ -1,0 +1,89 @@
+// Tile planner and persistent tile scheduler shared by the grouped GEMMs.
+//
+// Expert grouped GEMMs see skewed routing: per-expert token counts differ by
+// 40x or more, and some experts are empty ("Composer 2 Technical Report",
+// section 6.1: the expert grouped GEMM gets more efficient with more tokens
+// per rank; the 384-expert, top-8 MoE class of "Scaling and Optimizing
+// Frontier Model Training").  The counts live on the device (`offsets`), so
+// the host cannot size the launch; instead:
+//  1. k_plan (one workgroup) reads offsets, validates them, orders the experts
+//     (by index, or longest-reduction-first when a tile's cost grows with the
+//     expert's token count) and writes per-expert tile prefix sums into the
+//     workspace, zeroing the claim counters;
+//  2. the GEMM runs a persistent grid (one workgroup per CU).  Tiles are dealt
+//     round-robin to the 8 XCDs (tile t belongs to XCD t % 8) and claimed
+//     through one atomic counter per XCD; a workgroup first drains its own
+//     XCD's queue (so tiles sharing an operand panel share that XCD's L2) and
+//     then steals from the others, which balances the tail.
+// Each output tile is computed by exactly one workgroup in a fixed k order:
+// results do not depend on which workgroup runs it (deterministic, batch
+// invariant; no split-K, no float atomics).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsq {
+
+constexpr int PLAN_HDR = 16;      // int32 words before the per-expert arrays
+constexpr int PLAN_CTR = 0;       // [0, 8): per-XCD claim counters
+constexpr int PLAN_TOTAL = 8;     // total tiles
+constexpr int PLAN_ERR = 9;       // 1 = invalid offsets (no work done)
+constexpr int MAX_EXPERTS = 4096;
+
+enum PlanMode { PLAN_RAGGED_ROWS = 0, PLAN_RAGGED_REDUCTION = 1 };
+
+// int32 words of one plan: header + tile_start[E+1] + order[E].
+__host__ __device__ inline int64_t plan_words(int E) { return PLAN_HDR + 2 * (int64_t)E + 1; }
+
+__device__ __forceinline__ const int32_t* plan_start(const int32_t* plan) { return plan + PLAN_HDR; }
+__device__ __forceinline__ const int32_t* plan_order(const int32_t* plan, int E) { return plan + PLAN_HDR + E + 1; }
+
+// Claim the next tile for this workgroup (thread 0 only).  Returns -1 when
+// every queue is drained.  `d` is the number of queues already found empty.
+__device__ __forceinline__ int claim_tile(int32_t* plan, int xcd, int total, int& d) {
+    while (d < 8) {
+        const int q = (xcd + d) & 7;
+        const int c = atomicAdd(&plan[PLAN_CTR + q], 1);
+        const int t = q + 8 * c;
+        if (t < total) return t;
+        ++d;
+    }
+    return -1;
+}
+
+// Position of tile t in the expert order: last i with tile_start[i] <= t
+// (empty experts have tile_start[i] == tile_start[i+1] and are skipped).
+__device__ __forceinline__ int find_position(const int32_t* start, int E, int t) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (start[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Arguments of the MXFP8 backward GEMM kernel (one launch computes either the
+// dgrad or the wgrad tiles).
+struct BwdArgs {
+    const uint8_t* dy_codes; const uint8_t* dy_scale;    // dgrad A: ROWWISE dY [M][N]
+    const uint8_t* wt_codes; const uint8_t* wt_scale;    // dgrad B: COLWISE_T W -> [K][Pw]
+    const uint8_t* dyt_codes; const uint8_t* dyt_scale;  // wgrad A: COLWISE_T dY -> [N][P]
+    const uint8_t* xt_codes; const uint8_t* xt_scale;    // wgrad B: COLWISE_T X -> [K][P]
+    const int32_t* offsets; int E; int64_t m_total; int64_t N; int64_t K;
+    int64_t P;   // padded token columns of the COLWISE_T activations
+    int64_t Pw;  // padded columns of the COLWISE_T weights
+    void* out; int out_f32;
+    int wgrad;   // 0: dgrad tiles, 1: wgrad tiles
+    int32_t* plan;
+};
+
+hipError_t launch_plan(const int32_t* offsets, int E, int64_t m_total, int mode, int bm, int nt, int kt,
+                       int32_t* plan, hipStream_t s);
+hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s);
+hipError_t launch_gemm_fwd_nvfp4v(const uint8_t* a_codes, const uint8_t* a_bscale, const float* a_rscale,
+                                  const uint8_t* w_codes, const uint8_t* w_bscale, const float* w_rscale,
+                                  const int32_t* offsets, int E, int64_t m_total, int64_t N, int64_t K, void* y,
+                                  int y_f32, int32_t* plan, int grid, hipStream_t s);
+
+}  // namespace bsq

@@ -236,11 +236,13 @@ def grouped_gemm_fwd(a_q, w_q, offsets, rows=None) -> np.ndarray:
     return y
 
 
-def grouped_gemm_dgrad(dy_q, wt_q, offsets, n, rows=None) -> np.ndarray:
+def grouped_gemm_dgrad(dy_q, wt_q, offsets, n, rows=None, absolute=False) -> np.ndarray:
     """dX[m, k] = sum_n dY_hat[m, n] * W_hat_e[n, k] (float64).
 
     ``dy_q`` = ROWWISE MXFP8 of dY [M, N]; ``wt_q`` = COLWISE_T MXFP8 of the
     weights [E*N, K] with segments of N rows per expert, i.e. codes [K, P_w].
+    ``absolute=True`` returns sum_n |dY_hat| |W_hat| instead (the scale of the
+    rounding error of any summation of these products).
     """
     off = np.asarray(offsets, np.int64)
     E = len(off) - 1
@@ -256,16 +258,19 @@ def grouped_gemm_dgrad(dy_q, wt_q, offsets, n, rows=None) -> np.ndarray:
         dy_hat = dequant_mxfp8(dy_q[0][r], dy_q[1][r])
         c0 = segment_start(int(e), woff)
         wt_hat = dequant_mxfp8(wt_q[0][:, c0:c0 + n], wt_q[1][:, c0 // 32:c0 // 32 + n // 32])
+        if absolute:
+            dy_hat, wt_hat = np.abs(dy_hat), np.abs(wt_hat)
         out[sel] = dy_hat @ wt_hat.T
     return out
 
 
-def grouped_gemm_wgrad(dyt_q, xt_q, offsets, experts=None) -> dict:
+def grouped_gemm_wgrad(dyt_q, xt_q, offsets, experts=None, absolute=False) -> dict:
     """dW_e[n, k] = sum_{m in segment e} dY_hat[m, n] * X_hat[m, k] (float64).
 
     ``dyt_q`` / ``xt_q`` = COLWISE_T MXFP8 of dY [M, N] and X [M, K] with the
     expert offsets.  Returns {e: dW_e [N, K]} for the listed (default: all)
-    experts; an empty expert gives zeros.
+    experts; an empty expert gives zeros.  ``absolute=True``: sums of
+    absolute products instead.
     """
     off = np.asarray(offsets, np.int64)
     E = len(off) - 1
@@ -277,6 +282,8 @@ def grouped_gemm_wgrad(dyt_q, xt_q, offsets, experts=None) -> dict:
         L = 32 * ((m_e + 31) // 32)
         dyt = dequant_mxfp8(dyt_q[0][:, c0:c0 + L], dyt_q[1][:, c0 // 32:c0 // 32 + L // 32])
         xt = dequant_mxfp8(xt_q[0][:, c0:c0 + L], xt_q[1][:, c0 // 32:c0 // 32 + L // 32])
+        if absolute:
+            dyt, xt = np.abs(dyt), np.abs(xt)
         res[int(e)] = dyt @ xt.T
     return res
 

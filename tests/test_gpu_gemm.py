@@ -1,0 +1,300 @@
+"""GPU parity of the grouped GEMMs through the C ABI against the CPU oracle
+(float64 over the dequantized operands).
+
+Tolerance: the GEMMs must be within max relative error 2e-3 of the oracle's
+float64 result r on the same quantized operands, read per expert as
+    max |y - r| / max |r| <= 2e-3                     (all GEMMs, fp32 outputs)
+and, where the matrix core accumulates in full fp32 (the forward's fp16
+MFMA), also element by element with a small-magnitude floor:
+    max |y - r| / max(|r|, 0.01 * rms_e(r)) <= 2e-3   (forward).
+The block-scaled fp8 MFMA of the backward sums the products of one
+instruction in a fixed-point window aligned to the largest product (measured
+on gfx950: errors ~2^-16 of sum|products| on random data, up to ~2^-12.3 when
+one product dwarfs the others), so the backward is additionally held to that
+window element by element:  |y - r| <= 2^-11 * sum_k |a_k b_k|.
+With bf16 outputs every element must be the round-to-nearest-even bf16 of the
+kernel's own fp32 value.
+Operands handed to the oracle are quantized by the oracle itself from the same
+seeded bf16 inputs (never taken from the GPU path); the GPU's quantized bytes
+are asserted equal first, so both GEMMs see identical operands.
+"""
+import numpy as np
+import pytest
+import torch
+
+from workloads import (CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, make_quantize_input, moe_counts,
+                       normal_bf16, offsets_from_counts, rng_for)
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _bf16_dev(bits):
+    return _to_dev(np.ascontiguousarray(bits).view(np.int16))
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _bits(t):
+    """bf16 device tensor -> numpy uint16 bit patterns."""
+    return _np(t.contiguous().view(torch.int16)).view(np.uint16)
+
+
+def rel_err(y, r):
+    rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
+    den = np.maximum(np.abs(r), 0.01 * rms)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(np.abs(y - r) / den)) if r.size else 0.0
+
+
+def max_rel_err(y, r):
+    m = np.abs(r).max() if r.size else 0.0
+    return float(np.abs(y - r).max() / m) if m > 0 else float(np.abs(y).max())
+
+
+def check_groups(y, r, groups, strict=True, absum=None):
+    """groups: list of (name, row index array into y/r)."""
+    for name, idx in groups:
+        if len(idx) == 0:
+            continue
+        assert max_rel_err(y[idx], r[idx]) <= TOL, (name, max_rel_err(y[idx], r[idx]))
+        if strict:
+            e = rel_err(y[idx], r[idx])
+            assert e <= TOL, (name, e)
+    if absum is not None:
+        assert np.all(np.abs(y - r) <= 2.0 ** -11 * absum), float(np.max(np.abs(y - r) / np.maximum(absum, 1e-300)))
+
+
+def bf16_rne(f32):
+    return f32_to_bf16_bits(np.asarray(f32, np.float32))
+
+
+# ------------------------------------------------------------- forward
+
+def _fwd_case(orc, bsq, counts, n, k, seed):
+    rng = rng_for(3, salt=seed)
+    off = offsets_from_counts(counts)
+    M, E = int(off[-1]), len(counts)
+    x = make_quantize_input(rng, M, k)
+    w = normal_bf16(rng, (E * n, k), 0.02)
+    a_q = orc.quantize_nvfp4v(x)
+    w_q = orc.quantize_nvfp4v(w)
+    a_d = bsq.bsq_quantize_nvfp4v(_bf16_dev(x))
+    w_d = bsq.bsq_quantize_nvfp4v(_bf16_dev(w))
+    for r, g in zip(a_q + w_q, a_d + w_d):
+        assert np.array_equal(r.view(np.uint8), _np(g).view(np.uint8))
+    offd = _to_dev(off)
+    y32 = bsq.bsq_grouped_gemm_fwd(a_d, w_d, offd, n, k, y_dtype=bsq.BSQ_F32)
+    y16 = bsq.bsq_grouped_gemm_fwd(a_d, w_d, offd, n, k, y_dtype=bsq.BSQ_BF16)
+    ref = orc.grouped_gemm_fwd(a_q, w_q, off)
+    y32n = _np(y32)
+    check_groups(y32n.astype(np.float64), ref, [(f"expert{e}", np.arange(off[e], off[e + 1])) for e in range(E)])
+    assert np.array_equal(_bits(y16), bf16_rne(y32n))
+    return y32n
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    ([300, 0, 17, 1, 256, 513], 256, 256),      # ragged, empty, one-token experts, several tiles
+    ([1000], 512, 1024),                        # one expert = dense GEMM
+    ([40, 70, 9], 264, 64),                     # n not a tile multiple, k = one chunk
+    ([129, 255, 257], 128, 448),                # k % 128 == 64 tail stage
+])
+def test_fwd_parity(orc, bsq_gpu, counts, n, k):
+    _fwd_case(orc, bsq_gpu, counts, n, k, seed=n + k)
+
+
+def test_fwd_deterministic(orc, bsq_gpu):
+    a = _fwd_case(orc, bsq_gpu, [200, 333, 0, 90], 256, 512, seed=11)
+    b = _fwd_case(orc, bsq_gpu, [200, 333, 0, 90], 256, 512, seed=11)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_fwd_tiny_moe_end_to_end(orc, bsq_gpu):
+    """Config 1: quantize -> gate/up -> SwiGLU -> quantize -> down.  Each GEMM
+    is checked against the oracle on identical operands; the activation H fed
+    to the down GEMM is computed by the harness from the oracle's gate/up
+    output (bf16-rounded), so no oracle input comes from the GPU path."""
+    from workloads import tiny_moe
+    d = tiny_moe()
+    off = d["offsets"]
+    E, H, I = 4, 256, 128
+    x, wgu, wdn = d["x_sorted"], d["w_gu"].reshape(E * 2 * I, H), d["w_down"].reshape(E * H, I)
+    offd = _to_dev(off)
+    a_q, wgu_q = orc.quantize_nvfp4v(x), orc.quantize_nvfp4v(wgu)
+    gu_ref = orc.grouped_gemm_fwd(a_q, wgu_q, off)
+    a_d, wgu_d = bsq_gpu.bsq_quantize_nvfp4v(_bf16_dev(x)), bsq_gpu.bsq_quantize_nvfp4v(_bf16_dev(wgu))
+    gu = _np(bsq_gpu.bsq_grouped_gemm_fwd(a_d, wgu_d, offd, 2 * I, H, y_dtype=bsq_gpu.BSQ_F32))
+    check_groups(gu.astype(np.float64), gu_ref, [(e, np.arange(off[e], off[e + 1])) for e in range(E)])
+    h = bf16_rne(orc.swiglu(bf16_bits_to_f32(bf16_rne(gu_ref)).astype(np.float64)))
+    h_q, wdn_q = orc.quantize_nvfp4v(h), orc.quantize_nvfp4v(wdn)
+    y_ref = orc.grouped_gemm_fwd(h_q, wdn_q, off)
+    h_d, wdn_d = bsq_gpu.bsq_quantize_nvfp4v(_bf16_dev(h)), bsq_gpu.bsq_quantize_nvfp4v(_bf16_dev(wdn))
+    for r, g in zip(h_q, h_d):
+        assert np.array_equal(r.view(np.uint8), _np(g).view(np.uint8))
+    y = _np(bsq_gpu.bsq_grouped_gemm_fwd(h_d, wdn_d, offd, H, I, y_dtype=bsq_gpu.BSQ_F32))
+    check_groups(y.astype(np.float64), y_ref, [(e, np.arange(off[e], off[e + 1])) for e in range(E)])
+
+
+def _sampled_rows(off, rng, first=4, last=4, rand=8):
+    out = []
+    for e in range(len(off) - 1):
+        m0, m1 = int(off[e]), int(off[e + 1])
+        if m1 == m0:
+            continue
+        idx = np.concatenate([np.arange(m0, min(m1, m0 + first)), np.arange(max(m0, m1 - last), m1),
+                              rng.integers(m0, m1, rand)])
+        out.append((e, np.unique(idx)))
+    return out
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_fwd_full_size_sampled(orc, bsq_gpu, which):
+    """Config 3 shapes at full size (32 experts, Zipf(1.1) over 32768 slots,
+    hidden 7168, intermediate 2048), launched exactly as the bench does; the
+    oracle checks sampled rows x sampled output channels of every expert."""
+    cfg = CONFIGS[3]
+    counts = moe_counts(cfg)
+    off = offsets_from_counts(counts)
+    E = cfg.n_experts
+    n, k = (2 * cfg.inter, cfg.hidden) if which == "gate_up" else (cfg.hidden, cfg.inter)
+    gen = torch.Generator(device="cuda").manual_seed(3003 if which == "gate_up" else 3004)
+    x = torch.randn((cfg.m_total, k), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((E * n, k), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    a_d, w_d = bsq_gpu.bsq_quantize_nvfp4v(x), bsq_gpu.bsq_quantize_nvfp4v(w)
+    y = bsq_gpu.bsq_grouped_gemm_fwd(a_d, w_d, _to_dev(off), n, k, y_dtype=bsq_gpu.BSQ_F32)
+    rng = rng_for(3, salt=17)
+    cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 30, replace=False)]))
+    for e, rows in _sampled_rows(off, rng):
+        xa = _bits(x[torch.from_numpy(rows).cuda()])
+        wr = _bits(w[torch.from_numpy(e * n + cols).cuda()])
+        a_q, w_q = orc.quantize_nvfp4v(xa), orc.quantize_nvfp4v(wr)
+        for r, g in zip(a_q, a_d):
+            assert np.array_equal(r.view(np.uint8), _np(g[torch.from_numpy(rows).cuda()]).view(np.uint8))
+        ref = orc.grouped_gemm_fwd(a_q, w_q, np.array([0, len(rows)], np.int32))
+        got = _np(y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]).astype(np.float64)
+        assert rel_err(got, ref) <= TOL and max_rel_err(got, ref) <= TOL, e
+
+
+# ------------------------------------------------------------- backward
+
+def _bwd_case(orc, bsq, counts, n, k, seed, dw_dtype=None):
+    rng = rng_for(4, salt=seed)
+    off = offsets_from_counts(counts)
+    M, E = int(off[-1]), len(counts)
+    dy = normal_bf16(rng, (M, n), 1e-3)
+    x = make_quantize_input(rng, M, k)
+    w = normal_bf16(rng, (E * n, k), 0.02)
+    woff = (np.arange(E + 1) * n).astype(np.int32)
+    dy_q = orc.quantize_mxfp8_rowwise(dy)
+    wt_q = orc.quantize_mxfp8_colwise_t(w, woff)
+    dyt_q = orc.quantize_mxfp8_colwise_t(dy, off)
+    xt_q = orc.quantize_mxfp8_colwise_t(x, off)
+    offd = _to_dev(off)
+    dy_d = bsq.bsq_quantize_mxfp8(_bf16_dev(dy), bsq.BSQ_ROWWISE)
+    wt_d = bsq.bsq_quantize_mxfp8(_bf16_dev(w), bsq.BSQ_COLWISE_T, offsets=_to_dev(woff))
+    dyt_d = bsq.bsq_quantize_mxfp8(_bf16_dev(dy), bsq.BSQ_COLWISE_T, offsets=offd)
+    xt_d = bsq.bsq_quantize_mxfp8(_bf16_dev(x), bsq.BSQ_COLWISE_T, offsets=offd)
+    for r, g in zip(dy_q + wt_q + dyt_q + xt_q, dy_d + wt_d + dyt_d + xt_d):
+        assert np.array_equal(r, _np(g))
+    dx32, dw32 = bsq.bsq_grouped_gemm_bwd(offd, M, n, k, dy_d, wt_d, dyt_d, xt_d, dx_dtype=bsq.BSQ_F32,
+                                          dw_dtype=bsq.BSQ_F32)
+    dx16, dw16 = bsq.bsq_grouped_gemm_bwd(offd, M, n, k, dy_d, wt_d, dyt_d, xt_d)
+    dx_ref = orc.grouped_gemm_dgrad(dy_q, wt_q, off, n)
+    dx_abs = orc.grouped_gemm_dgrad(dy_q, wt_q, off, n, absolute=True)
+    dw_ref = orc.grouped_gemm_wgrad(dyt_q, xt_q, off)
+    dw_abs = orc.grouped_gemm_wgrad(dyt_q, xt_q, off, absolute=True)
+    if M:
+        dx32n = _np(dx32)
+        check_groups(dx32n.astype(np.float64), dx_ref, [(e, np.arange(off[e], off[e + 1])) for e in range(E)],
+                     strict=False, absum=dx_abs)
+        assert np.array_equal(_bits(dx16), bf16_rne(dx32n))
+    dw32n = _np(dw32)
+    for e in range(E):
+        check_groups(dw32n[e].astype(np.float64), dw_ref[e], [(e, np.arange(n))], strict=False, absum=dw_abs[e])
+        if counts[e] == 0:
+            assert not dw32n[e].any()
+    assert np.array_equal(_bits(dw16), bf16_rne(dw32n))
+    return dx32, dw32
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    ([300, 0, 17, 1, 256, 513], 256, 256),
+    ([1000], 512, 384),
+    ([40, 70, 9], 320, 64),
+    ([0, 0, 0], 128, 128),                      # all experts empty: dW = 0
+])
+def test_bwd_parity(orc, bsq_gpu, counts, n, k):
+    _bwd_case(orc, bsq_gpu, counts, n, k, seed=n + k)
+
+
+def test_bwd_deterministic(orc, bsq_gpu):
+    a = _bwd_case(orc, bsq_gpu, [200, 333, 0, 90], 256, 256, seed=12)
+    b = _bwd_case(orc, bsq_gpu, [200, 333, 0, 90], 256, 256, seed=12)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_bwd_full_size_sampled(orc, bsq_gpu):
+    """Config 4 (down projection: n = 7168, k = 2048) at full size: dgrad on
+    sampled rows of every expert; wgrad on sampled output rows of the two
+    smallest and the largest experts."""
+    cfg = CONFIGS[4]
+    counts = moe_counts(cfg)
+    off = offsets_from_counts(counts)
+    E, n, k, M = cfg.n_experts, cfg.hidden, cfg.inter, cfg.m_total
+    gen = torch.Generator(device="cuda").manual_seed(4004)
+    dy = (torch.randn((M, n), generator=gen, device="cuda") * 1e-3).to(torch.bfloat16)
+    h = torch.randn((M, k), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((E * n, k), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    offd = _to_dev(off)
+    woff = (np.arange(E + 1) * n).astype(np.int32)
+    dy_d = bsq_gpu.bsq_quantize_mxfp8(dy, bsq_gpu.BSQ_ROWWISE)
+    wt_d = bsq_gpu.bsq_quantize_mxfp8(w, bsq_gpu.BSQ_COLWISE_T, offsets=_to_dev(woff))
+    dyt_d = bsq_gpu.bsq_quantize_mxfp8(dy, bsq_gpu.BSQ_COLWISE_T, offsets=offd)
+    ht_d = bsq_gpu.bsq_quantize_mxfp8(h, bsq_gpu.BSQ_COLWISE_T, offsets=offd)
+    dx, dw = bsq_gpu.bsq_grouped_gemm_bwd(offd, M, n, k, dy_d, wt_d, dyt_d, ht_d, dx_dtype=bsq_gpu.BSQ_F32,
+                                          dw_dtype=bsq_gpu.BSQ_F32)
+    rng = rng_for(4, salt=19)
+    kcols = np.unique(np.concatenate([[0, k - 1], rng.choice(k, 30, replace=False)]))
+    for e, rows in _sampled_rows(off, rng, 2, 2, 4):
+        dy_q = orc.quantize_mxfp8_rowwise(_bits(dy[torch.from_numpy(rows).cuda()]))
+        w_e = _bits(w[e * n:(e + 1) * n][:, torch.from_numpy(kcols).cuda()])
+        wt_q = orc.quantize_mxfp8_colwise_t(w_e, np.array([0, n], np.int32))
+        seg = np.array([0, len(rows)], np.int32)
+        ref = orc.grouped_gemm_dgrad(dy_q, wt_q, seg, n)
+        absum = orc.grouped_gemm_dgrad(dy_q, wt_q, seg, n, absolute=True)
+        got = _np(dx[torch.from_numpy(rows).cuda()][:, torch.from_numpy(kcols).cuda()]).astype(np.float64)
+        check_groups(got, ref, [(("dgrad", e), np.arange(len(rows)))], strict=False, absum=absum)
+    order = np.argsort(counts, kind="stable")
+    nrows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 14, replace=False)]))
+    for e in [int(order[0]), int(order[1]), int(order[-1])]:
+        m0, m1 = int(off[e]), int(off[e + 1])
+        seg = np.array([0, m1 - m0], np.int32)
+        dyt_q = orc.quantize_mxfp8_colwise_t(_bits(dy[m0:m1][:, torch.from_numpy(nrows).cuda()]), seg)
+        ht_q = orc.quantize_mxfp8_colwise_t(_bits(h[m0:m1]), seg)
+        ref = orc.grouped_gemm_wgrad(dyt_q, ht_q, seg)[0]
+        absum = orc.grouped_gemm_wgrad(dyt_q, ht_q, seg, absolute=True)[0]
+        got = _np(dw[e][torch.from_numpy(nrows).cuda()]).astype(np.float64)
+        check_groups(got, ref, [(("wgrad", e), np.arange(len(nrows)))], strict=False, absum=absum)
+
+
+def test_invalid_offsets_reported(bsq_gpu):
+    """Decreasing offsets: the planner flags them and no tile runs."""
+    off = _to_dev(np.array([0, 50, 40, 64], np.int32))
+    a = bsq_gpu.bsq_quantize_nvfp4v(torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda"))
+    w = bsq_gpu.bsq_quantize_nvfp4v(torch.zeros((3 * 64, 128), dtype=torch.bfloat16, device="cuda"))
+    ws = torch.zeros(bsq_gpu.bsq_workspace_size(0, 3, 64, 64, 128), dtype=torch.uint8, device="cuda")
+    y = torch.full((64, 64), 7.0, device="cuda")
+    bsq_gpu.bsq_grouped_gemm_fwd(a, w, off, 64, 128, y_dtype=bsq_gpu.BSQ_F32, y=y, workspace=ws)
+    assert bsq_gpu.bsq_debug_status(ws) == 1
+    assert bool((y == 7.0).all())
+    good = _to_dev(np.array([0, 10, 40, 64], np.int32))
+    bsq_gpu.bsq_grouped_gemm_fwd(a, w, good, 64, 128, y_dtype=bsq_gpu.BSQ_F32, y=y, workspace=ws)
+    assert bsq_gpu.bsq_debug_status(ws) == 0
+    assert bool((y == 0.0).all())

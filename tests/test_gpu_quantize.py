@@ -1,0 +1,219 @@
+"""GPU parity of the quantizers through the C ABI: bit-exact codes, scale
+bytes and per-row fp32 scales against the CPU oracle on the same seeded bf16
+inputs, plus exhaustive sweeps of the device element encoders."""
+import numpy as np
+import pytest
+import torch
+
+from conftest import bf16
+from workloads import (bf16_bits_to_f32, make_quantize_input, normal_bf16, offsets_from_counts, rng_for,
+                       expert_counts_zipf)
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _bf16_dev(bits):
+    return _to_dev(bits.view(np.int16))
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------ exhaustive encoders
+
+def _breakpoints(encode, max_code):
+    """First fp32 bit pattern (>= 0) of each code of a monotone encoder, from
+    the oracle, by binary search over the non-negative bit patterns."""
+    def code_at(u):
+        return int(encode(np.array([u], np.uint32).view(np.float32))[0])
+    starts = [0]
+    codes = [code_at(0)]
+    lo_u = 0
+    while codes[-1] != max_code:
+        c = codes[-1]
+        lo, hi = lo_u, 0x7F800000  # code_at(hi) == max_code (inf saturates)
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            if code_at(mid) > c:
+                hi = mid
+            else:
+                lo = mid
+        starts.append(hi)
+        codes.append(code_at(hi))
+        lo_u = hi
+    return np.array(starts, np.int64), np.array(codes, np.int64)
+
+
+@pytest.mark.parametrize("which", ["e2m1", "e4m3"])
+def test_encoder_exhaustive_all_fp32(orc, bsq_gpu, which):
+    """Every non-NaN fp32 bit pattern, both signs, through the device encoder
+    the quantizers use, against runs derived from the oracle's encoder."""
+    if which == "e2m1":
+        enc, dev_enc, max_code, sign = orc.e2m1_encode, bsq_gpu.bsq_debug_encode_e2m1, 7, 8
+    else:
+        enc, dev_enc, max_code, sign = orc.e4m3_encode, bsq_gpu.bsq_debug_encode_e4m3, 0x7E, 0x80
+    starts, codes = _breakpoints(enc, max_code)
+    # monotone encoder: the runs are the whole truth (spot check them)
+    probe = np.concatenate([starts, np.maximum(starts - 1, 0)]).astype(np.uint32)
+    ref_probe = np.searchsorted(starts, probe.astype(np.int64), side="right") - 1
+    assert np.array_equal(enc(probe.view(np.float32)), codes[ref_probe].astype(np.uint8))
+    top = 0x7F800001  # +inf included, NaNs excluded
+    chunk = 1 << 27
+    starts_d = torch.from_numpy(starts).cuda()
+    codes_d = torch.from_numpy(codes).cuda().to(torch.uint8)
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    bad = 0
+    for s_bit in (0, 1 << 31):
+        for lo in range(0, top, chunk):
+            n = min(chunk, top - lo)
+            u = torch.arange(lo, lo + n, dtype=torch.int64, device="cuda")
+            v = u | s_bit                                   # unsigned 32-bit pattern
+            x = torch.where(v >= (1 << 31), v - (1 << 32), v).to(torch.int32).view(torch.float32)
+            dev_enc(x, out[:n])
+            idx = torch.searchsorted(starts_d, u, right=True) - 1
+            exp = codes_d[idx] | (sign if s_bit else 0)
+            bad += int((out[:n] != exp).sum())
+    assert bad == 0
+
+
+# ------------------------------------------------------------ NVFP4 variant
+
+def _nvfp4v_check(orc, bsq_gpu, x_bits):
+    ref = orc.quantize_nvfp4v(x_bits)
+    got = bsq_gpu.bsq_quantize_nvfp4v(_bf16_dev(x_bits))
+    for r, g, nm in zip(ref, got, ("codes", "bscale", "rscale")):
+        g = _np(g)
+        if nm == "rscale":
+            assert np.array_equal(r.view(np.uint32), g.view(np.uint32)), nm
+        else:
+            assert np.array_equal(r, g), (nm, np.argwhere(r != g)[:5])
+
+
+@pytest.mark.parametrize("cols", [16, 48, 256, 2048, 7168, 16384])
+def test_nvfp4v_parity_shapes(orc, bsq_gpu, cols):
+    rng = rng_for(2, salt=cols)
+    rows = 37 if cols >= 7168 else 133
+    _nvfp4v_check(orc, bsq_gpu, make_quantize_input(rng, rows, cols))
+
+
+def test_nvfp4v_parity_edge_values(orc, bsq_gpu):
+    rng = rng_for(2, salt=99)
+    x = normal_bf16(rng, (24, 256))
+    x[0] = 0                                     # zero row
+    x[1] = bf16(np.full(256, -0.0))              # negative-zero row
+    x[2, :16] = 0                                # zero block
+    x[3] = bf16(rng.standard_normal(256) * 2.0 ** 120)   # 448*a_b overflow path
+    x[4] = bf16(rng.standard_normal(256) * 2.0 ** -128)  # subnormal bf16 values
+    x[5, :] = bf16(np.full(256, 2.0 ** -133))    # smallest subnormal everywhere
+    x[6] = bf16(np.where(rng.random(256) < 0.5, 3.0e38, -1e-30))
+    golden = [2688, -1344, 112, 336, 560, 784, 1120, 1568, 2240, -56, 0, 1, -2688, 200, -200, 100]
+    x[7, :16] = bf16(golden)                     # every E2M1 tie
+    x[7, 16:] = bf16(np.tile(golden, 15) * 0.75)
+    x[8] = bf16(rng.standard_normal(256) * 2.0 ** -100)
+    x[9, ::16] = bf16(np.full(16, 1.0))          # one nonzero per block
+    x[9, 1::16] = bf16(np.full(16, 2.0 ** -12))
+    x[10] = bf16(rng.integers(-6, 7, 256) * 0.5)
+    _nvfp4v_check(orc, bsq_gpu, x)
+
+
+def test_nvfp4v_full_size_sampled_rows(orc, bsq_gpu):
+    """Config 2 at full size (16384 x 7168, outlier channels) in one launch;
+    the quantizer is row-local, so sampled rows are checked exactly."""
+    rng = rng_for(2)
+    x = make_quantize_input(rng, 16384, 7168)
+    got = bsq_gpu.bsq_quantize_nvfp4v(_bf16_dev(x))
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(16384 - 64, 16384),
+                                     rng.choice(16384, 256, replace=False)]))
+    ref = orc.quantize_nvfp4v(x[rows])
+    for r, g in zip(ref, got):
+        assert np.array_equal(r.view(np.uint8), _np(g)[rows].view(np.uint8))
+
+
+def test_nvfp4v_batch_invariance_gpu(bsq_gpu):
+    """A row quantized in any batch (shuffled, random batch sizes) gives the
+    same bytes: per-token scaling, no tensor-wide statistic."""
+    rng = rng_for(5, salt=3)
+    x = make_quantize_input(rng, 2048, 7168)
+    xd = _bf16_dev(x)
+    full = [_np(t) for t in bsq_gpu.bsq_quantize_nvfp4v(xd)]
+    for _ in range(16):
+        n = int(rng.integers(1, 2048))
+        sel = rng.permutation(2048)[:n]
+        part = bsq_gpu.bsq_quantize_nvfp4v(xd[torch.from_numpy(sel).cuda()].contiguous())
+        for f, p in zip(full, part):
+            assert np.array_equal(f[sel].view(np.uint8), _np(p).view(np.uint8))
+
+
+def test_nvfp4v_strided_input(orc, bsq_gpu):
+    rng = rng_for(2, salt=5)
+    big = make_quantize_input(rng, 40, 512)
+    xd = _bf16_dev(big)[:, 128:384]
+    got = bsq_gpu.bsq_quantize_nvfp4v(xd)
+    ref = orc.quantize_nvfp4v(np.ascontiguousarray(big[:, 128:384]))
+    for r, g in zip(ref, got):
+        assert np.array_equal(r.view(np.uint8), _np(g).view(np.uint8))
+
+
+# ------------------------------------------------------------------ MXFP8
+
+@pytest.mark.parametrize("cols", [32, 96, 2048, 7168])
+def test_mxfp8_rowwise_parity(orc, bsq_gpu, cols):
+    rng = rng_for(2, salt=100 + cols)
+    x = make_quantize_input(rng, 129, cols)
+    x[0] = 0
+    x[1, :32] = bf16(np.full(32, 2.0 ** -130))
+    x[2] = bf16(rng.standard_normal(cols) * 2.0 ** 125)
+    x[3] = bf16(rng.standard_normal(cols) * 1e-3)
+    x[4, :32] = bf16(np.array([3.875, -0.0] + [0.5] * 30))
+    rc, rs = orc.quantize_mxfp8_rowwise(x)
+    gc, gs = bsq_gpu.bsq_quantize_mxfp8(_bf16_dev(x), bsq_gpu.BSQ_ROWWISE)
+    assert np.array_equal(rc, _np(gc)) and np.array_equal(rs, _np(gs))
+
+
+@pytest.mark.parametrize("case", ["ragged", "empty_groups", "single", "weights"])
+def test_mxfp8_colwise_t_parity(orc, bsq_gpu, case):
+    rng = rng_for(4, salt=["ragged", "empty_groups", "single", "weights"].index(case))
+    if case == "ragged":
+        counts = [37, 0, 300, 1, 64, 95, 33]
+        cols = 264
+    elif case == "empty_groups":
+        counts = [0, 0, 70, 0, 0]
+        cols = 96
+    elif case == "single":
+        counts = [1000]
+        cols = 512
+    else:  # expert weights [E][N][K] as rows E*N with offsets multiples of N
+        counts = [128] * 4
+        cols = 256
+    off = offsets_from_counts(counts)
+    M = int(off[-1])
+    x = make_quantize_input(rng, M, cols) if M else np.zeros((0, cols), np.uint16)
+    rc, rs = orc.quantize_mxfp8_colwise_t(x, off)
+    gc, gs = bsq_gpu.bsq_quantize_mxfp8(_bf16_dev(x), bsq_gpu.BSQ_COLWISE_T, offsets=_to_dev(off))
+    assert np.array_equal(rc, _np(gc)), np.argwhere(rc != _np(gc))[:5]
+    assert np.array_equal(rs, _np(gs))
+
+
+def test_mxfp8_colwise_t_full_size_sampled(orc, bsq_gpu):
+    """dY-shaped input at full size (32768 x 7168, Zipf(1.1) over 32 experts):
+    the transposed layout is checked exactly on sampled channels (columns are
+    independent) for every expert segment, plus all padding bytes."""
+    from workloads import CONFIGS, moe_counts
+    counts = moe_counts(CONFIGS[4])
+    off = offsets_from_counts(counts)
+    gen = torch.Generator(device="cuda").manual_seed(1004)
+    dy = (torch.randn((32768, 7168), generator=gen, device="cuda") * 1e-3).to(torch.bfloat16)
+    gc, gs = bsq_gpu.bsq_quantize_mxfp8(dy, bsq_gpu.BSQ_COLWISE_T, offsets=_to_dev(off))
+    rng = rng_for(4, salt=7)
+    ch = np.unique(np.concatenate([[0, 7167], rng.choice(7168, 30, replace=False)]))
+    x_ch = _np(dy[:, torch.from_numpy(ch).cuda()].contiguous().view(torch.int16)).view(np.uint16)
+    rc, rs = orc.quantize_mxfp8_colwise_t(np.ascontiguousarray(x_ch), off)
+    gcn = _np(gc[torch.from_numpy(ch).cuda()])
+    gsn = _np(gs[torch.from_numpy(ch).cuda()])
+    assert np.array_equal(rc, gcn) and np.array_equal(rs, gsn)
