@@ -126,14 +126,14 @@ def bsq_quantize_nvfp4v(x, codes=None, bscale=None, rscale=None, offsets=None, s
 
 
 def bsq_quantize_mxfp8(x, axis=BSQ_ROWWISE, offsets=None, codes=None, scale=None, stream=None):
-    """MXFP8 quantization of bf16 ``x`` [rows, cols].
-    ROWWISE: (codes [rows, cols], scale [rows, cols/32]).
-    COLWISE_T (needs int32 device ``offsets``): (codes [cols, P], scale [cols, P/32])."""
+    """MXFP8 quantization of bf16 ``x`` [rows, cols]; scales are block-major.
+    ROWWISE: (codes [rows, cols], scale [cols/32, rows]).
+    COLWISE_T (needs int32 device ``offsets``): (codes [cols, P], scale [P/32, cols])."""
     _dev(x, "x", _BF16)
     rows, cols, ld = _rows_ld(x)
     dev = x.device
     if axis == BSQ_ROWWISE:
-        shapes = ((rows, cols), (rows, cols // 32))
+        shapes = ((rows, cols), (cols // 32, rows))
         ng = 0
     else:
         if offsets is None:
@@ -141,7 +141,7 @@ def bsq_quantize_mxfp8(x, axis=BSQ_ROWWISE, offsets=None, codes=None, scale=None
         _dev(offsets, "offsets", (torch.int32,))
         ng = offsets.numel() - 1
         Pc = bsq_colwise_padded_cols(ng, rows)
-        shapes = ((cols, Pc), (cols, Pc // 32))
+        shapes = ((cols, Pc), (Pc // 32, cols))
     codes = torch.empty(shapes[0], dtype=torch.uint8, device=dev) if codes is None else codes
     scale = torch.empty(shapes[1], dtype=torch.uint8, device=dev) if scale is None else scale
     for t, nm, shape in ((codes, "codes", shapes[0]), (scale, "scale", shapes[1])):

@@ -159,8 +159,11 @@ bsq_status bsq_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_scale
     if (wg && (!aligned(dyt_codes, 16) || !aligned(xt_codes, 16))) return BSQ_ERR_UNSUPPORTED;
     const int64_t P = bsq_colwise_padded_cols(num_experts, m_total);
     const int64_t Pw = bsq_colwise_padded_cols(num_experts, (int64_t)num_experts * n);
+    // per-tile buffer offsets are 32-bit: 256 rows of codes, and block-major
+    // scale runs (block index x rows of the scale matrix)
     if (256 * Pw + Pw >= kMaxBufferOffset || 256 * P + P >= kMaxBufferOffset || 256 * n >= kMaxBufferOffset ||
-        m_total >= (int64_t)1 << 31)
+        m_total >= (int64_t)1 << 31 || (n / 32 + 1) * (m_total + 256) >= kMaxBufferOffset ||
+        (P / 32 + 1) * (n + k) >= kMaxBufferOffset || (Pw / 32 + 1) * k >= kMaxBufferOffset)
         return BSQ_ERR_UNSUPPORTED;
     if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_BWD, num_experts, m_total, n, k))
         return BSQ_ERR_WORKSPACE_TOO_SMALL;

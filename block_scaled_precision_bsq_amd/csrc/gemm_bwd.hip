@@ -22,26 +22,30 @@
 // g: memory order is the hardware k order.
 //
 // Tiling: 256 x 256 outputs per workgroup (4 waves, 2 x 2, 128 x 128 each:
-// 4 x 4 MFMA tiles, fp32 accumulators in AGPRs); 128-byte k stages double
-// buffered in LDS, rows padded to 144 bytes (16-lane 16-byte reads hit
-// distinct banks), next stage prefetched into registers during the MFMAs.
+// 4 x 4 MFMA tiles, fp32 accumulators in AGPRs).  k runs in 64-byte stages
+// (one MFMA k step) through a 4-deep LDS ring filled by buffer-to-LDS DMA
+// (gemm_pipe.h): three stages are in flight while one is multiplied, and the
+// fragments of stage s+1 are read from LDS into a second register set while
+// the MFMAs of stage s run.
 #include "device_common.h"
 #include "gemm_common.h"
+#include "gemm_pipe.h"
+
+#include <type_traits>
+#include <stddef.h>
 
 namespace bsq {
 
 constexpr int BWD_BM = 256;
 constexpr int BWD_BN = 256;
-constexpr int BWD_BK = 128;             // k bytes (= elements) per stage
-constexpr int BWD_PITCH = BWD_BK + 16;  // padded LDS row (bytes)
+constexpr int BWD_DMA_PER_STAGE = 12;  // DMA instructions per wave per stage
 
 struct BwdSmem {
-    uint8_t a[2][BWD_BM * BWD_PITCH];
-    uint8_t b[2][BWD_BN * BWD_PITCH];
-    uint32_t sa[2][BWD_BM];  // 4 scale bytes (blocks of the stage) per row
-    uint32_t sb[2][BWD_BN];
+    uint8_t a[PIPE_NST][PIPE_STAGE_BYTES];
+    uint8_t b[PIPE_NST][PIPE_STAGE_BYTES];
+    uint32_t sa[PIPE_NST][PIPE_ROWS * 2];  // E8M0 byte of (block, row) in dword block*256 + row
+    uint32_t sb[PIPE_NST][PIPE_ROWS * 2];
 };
-
 
 // One output tile of C[i][j] = sum_r A[i][r] B[j][r].
 struct TileOps {
@@ -51,21 +55,55 @@ struct TileOps {
     char* c; int64_t ldc;
 };
 
+struct BwdFrag {
+    int8v a[4], b[4];
+    int sa[4], sb[4];
+};
+
+template <int V> using IC = std::integral_constant<int, V>;
+
+template <bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
-    BwdSmem& sm = *reinterpret_cast<BwdSmem*>(smem_raw);
     __shared__ int s_tile;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler keep
+    // everything derived from it in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int lr = lane & 31, g = lane >> 5;
     const int xcd = blockIdx.x & 7;
-    const int esz = p.out_f32 ? 4 : 2;
+    constexpr int esz = OUT_F32 ? 4 : 2;
     const int total = p.plan[PLAN_TOTAL];
     const int32_t* start = plan_start(p.plan);
     const int32_t* order = plan_order(p.plan, p.E);
     int dq = 0;
+
+    // 32-bit LDS byte addresses of the ring buffers
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
+    const uint32_t LA = lds0 + offsetof(BwdSmem, a), LB = lds0 + offsetof(BwdSmem, b);
+    const uint32_t LSA = lds0 + offsetof(BwdSmem, sa), LSB = lds0 + offsetof(BwdSmem, sb);
+    // fragment reads address the same buffers relative to smem_raw
+    const __attribute__((address_space(3))) uint8_t* lds =
+        (const __attribute__((address_space(3))) uint8_t*)(smem_raw);
+
+    // DMA lane geometry (tile-invariant): instruction i of this wave covers
+    // rows 16 * (4 * wave + i) + lane / 4; the lane fetches logical chunk
+    // (lane & 3) ^ swz(row) of its row into slot lane & 3.  swz(row) depends
+    // only on bits 1..3 of the row, i.e. on lane / 4.
+    const int drow0 = 64 * wave + (lane >> 2);
+    const uint32_t dchunk = (uint32_t)((lane & 3) ^ swz(lane >> 2));
+    const bool dlow = dchunk < 2;  // chunk lies in the first 32-byte k block
+    // Fragment read geometry: lane (lr, g) reads chunks g and g + 2 of row
+    // lr of each 32-row group; swz(row) = swz(lr) for every such row.
+    const uint32_t fr0 = (uint32_t)(lr * PIPE_BK + 16 * (g ^ swz(lr)));
+    const uint32_t fr1 = fr0 ^ 32u;  // chunk g + 2
+    const uint32_t fa = offsetof(BwdSmem, a) + (uint32_t)(wm * 128 * PIPE_BK);
+    const uint32_t fb = offsetof(BwdSmem, b) + (uint32_t)(wn * 128 * PIPE_BK);
+    const uint32_t fsa = offsetof(BwdSmem, sa) + 4u * (uint32_t)(256 * g + wm * 128 + lr);
+    const uint32_t fsb = offsetof(BwdSmem, sb) + 4u * (uint32_t)(256 * g + wn * 128 + lr);
 
     for (;;) {
         if (tid == 0) s_tile = claim_tile(p.plan, xcd, total, dq);
@@ -75,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         if (tile < 0) break;
 
         // Tile decode; readfirstlane marks the results wave-uniform so that
-        // addresses and buffer resources stay in SGPRs.
+        // addresses and buffer descriptors stay in SGPRs.
         const int pos = find_position(start, p.E, tile);
         const int e = __builtin_amdgcn_readfirstlane(order[pos]);
         const int local = __builtin_amdgcn_readfirstlane(tile - start[pos]);
@@ -85,25 +123,28 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         if (!p.wgrad) {
             // dX[m][k] = sum_n dY[m][n] Wt_e[k][n]
             const int KT = (int)((p.K + BWD_BN - 1) / BWD_BN);
-            const int mt = local / KT, kt = local % KT;
+            int mt, kt;
+            grouped_tile(local, (int)((off1 - off0 + BWD_BM - 1) / BWD_BM), KT, mt, kt);
             const int64_t m0 = off0 + (int64_t)mt * BWD_BM, k0 = (int64_t)kt * BWD_BN;
             const int64_t cw = (int64_t)e * (p.N + 32);  // 32*(e + e*N/32): segment start of W_e
-            op.a = p.dy_codes + m0 * p.N; op.as = p.dy_scale + m0 * (p.N / 32);
-            op.lda = p.N; op.ldas = p.N / 32; op.rows_a = (int)min((int64_t)BWD_BM, off1 - m0);
-            op.b = p.wt_codes + k0 * p.Pw + cw; op.bs = p.wt_scale + k0 * (p.Pw / 32) + cw / 32;
-            op.ldb = p.Pw; op.ldbs = p.Pw / 32; op.rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
+            // block-major scales: block j of rows r0.. starts at base + j * rows_total + r0
+            op.a = p.dy_codes + m0 * p.N; op.as = p.dy_scale + m0;
+            op.lda = p.N; op.ldas = p.m_total; op.rows_a = (int)min((int64_t)BWD_BM, off1 - m0);
+            op.b = p.wt_codes + k0 * p.Pw + cw; op.bs = p.wt_scale + (cw / 32) * p.K + k0;
+            op.ldb = p.Pw; op.ldbs = p.K; op.rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
             op.R = p.N;
             op.c = reinterpret_cast<char*>(p.out) + (m0 * p.K + k0) * esz; op.ldc = p.K;
         } else {
             // dW_e[n][k] = sum_{m in e} dY^T[n][m] X^T[k][m]
             const int KT = (int)((p.K + BWD_BN - 1) / BWD_BN);
-            const int nt = local / KT, kt = local % KT;
+            int nt, kt;
+            grouped_tile(local, (int)((p.N + BWD_BM - 1) / BWD_BM), KT, nt, kt);
             const int64_t n0 = (int64_t)nt * BWD_BM, k0 = (int64_t)kt * BWD_BN;
             const int64_t c0 = 32 * ((int64_t)e + off0 / 32);  // segment start column
-            op.a = p.dyt_codes + n0 * p.P + c0; op.as = p.dyt_scale + n0 * (p.P / 32) + c0 / 32;
-            op.lda = p.P; op.ldas = p.P / 32; op.rows_a = (int)min((int64_t)BWD_BM, p.N - n0);
-            op.b = p.xt_codes + k0 * p.P + c0; op.bs = p.xt_scale + k0 * (p.P / 32) + c0 / 32;
-            op.ldb = p.P; op.ldbs = p.P / 32; op.rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
+            op.a = p.dyt_codes + n0 * p.P + c0; op.as = p.dyt_scale + (c0 / 32) * p.N + n0;
+            op.lda = p.P; op.ldas = p.N; op.rows_a = (int)min((int64_t)BWD_BM, p.N - n0);
+            op.b = p.xt_codes + k0 * p.P + c0; op.bs = p.xt_scale + (c0 / 32) * p.K + k0;
+            op.ldb = p.P; op.ldbs = p.K; op.rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
             op.R = 32 * ((off1 - off0 + 31) / 32);
             op.c = reinterpret_cast<char*>(p.out) + (((int64_t)e * p.N + n0) * p.K + k0) * esz; op.ldc = p.K;
         }
@@ -115,51 +156,83 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         op.ldc = uniform_i64(op.ldc); op.R = uniform_i64(op.R);
         op.rows_a = __builtin_amdgcn_readfirstlane(op.rows_a);
         op.rows_b = __builtin_amdgcn_readfirstlane(op.rows_b);
-        const int nstages = (int)((op.R + BWD_BK - 1) / BWD_BK);
+        const int nstages = (int)((op.R + PIPE_BK - 1) / PIPE_BK);
 
-        uint4 ra[8], rb[8];
-        uint32_t rsa, rsb;
-        const __amdgpu_buffer_rsrc_t rA = make_rsrc(op.a, 0x7FFFFFFFu);
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(op.b, 0x7FFFFFFFu);
-        const __amdgpu_buffer_rsrc_t rAs = make_rsrc(op.as, 0x7FFFFFFFu);
-        const __amdgpu_buffer_rsrc_t rBs = make_rsrc(op.bs, 0x7FFFFFFFu);
+        const i32x4 dA = make_desc(op.a), dB = make_desc(op.b);
+        const i32x4 dAs = make_desc(op.as), dBs = make_desc(op.bs);
         const uint32_t lda = (uint32_t)op.lda, ldb = (uint32_t)op.ldb;
         const uint32_t ldas = (uint32_t)op.ldas, ldbs = (uint32_t)op.ldbs;
         const uint32_t R = (uint32_t)op.R;
-        auto load_stage = [&](int s) {
-            const uint32_t q = tid & 7;
-            const uint32_t kb = (uint32_t)s * BWD_BK + 16 * q;
-            const bool okk = kb < R;
+
+        // Per-tile lane offsets at k = 0; rows past the tile read as zero.
+        uint32_t va[4], vb[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = (tid >> 3) + 32 * i;
-                ra[i] = buf_load16(rA, (okk && r < op.rows_a) ? r * lda + kb : OOB);
-                rb[i] = buf_load16(rB, (okk && r < op.rows_b) ? r * ldb + kb : OOB);
-            }
-            // 4 scale bytes per row (row = tid); byte loads: the scale row
-            // pitch need not be 4-byte aligned.
-            const uint32_t sblk = (uint32_t)s * (BWD_BK / 32);
-            const uint32_t nblk = R / 32;
-            uint32_t va = 0, vb = 0;
+        for (int i = 0; i < 4; ++i) {
+            const int row = drow0 + 16 * i;
+            va[i] = row < op.rows_a ? (uint32_t)row * lda + 16 * dchunk : OOB;
+            vb[i] = row < op.rows_b ? (uint32_t)row * ldb + 16 * dchunk : OOB;
+        }
+        // scales: instruction i (of 2) covers k block (2 * wave + i) >> 2 of
+        // the stage, rows 64 * ((2 * wave + i) & 3) + lane
+        uint32_t vsa[2], vsb[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool okb = sblk + j < nblk;
-                va |= buf_load1(rAs, (okb && tid < op.rows_a) ? tid * ldas + sblk + j : OOB) << (8 * j);
-                vb |= buf_load1(rBs, (okb && tid < op.rows_b) ? tid * ldbs + sblk + j : OOB) << (8 * j);
+        for (int i = 0; i < 2; ++i) {
+            const int ins = 2 * wave + i;
+            const int row = 64 * (ins & 3) + lane;
+            const uint32_t kb = (uint32_t)(ins >> 2);
+            vsa[i] = row < op.rows_a ? kb * ldas + row : OOB;
+            vsb[i] = row < op.rows_b ? kb * ldbs + row : OOB;
+        }
+
+        // DMA of stage st into ring slot st % 4: 12 instructions per wave,
+        // issued in 5 parts (part i < 4: A and B rows of instruction i; part
+        // 4: the four scale instructions).  Stages past the end land as
+        // zeros, which keeps the per-stage instruction count, and so the
+        // vmcnt bookkeeping, uniform.  R is a multiple of 32: a stage is
+        // either whole, half (its first k block only) or past the end.
+        auto issue_part = [&](int st, int part) {
+            const uint32_t q = (uint32_t)st & (PIPE_NST - 1);
+            const uint32_t kbase = (uint32_t)st * PIPE_BK;
+            if (part < 4) {
+                const bool full = kbase + PIPE_BK <= R;
+                const bool half = kbase + 32 == R;
+                const bool okc = full | (half & dlow);
+                const uint32_t ldst = q * PIPE_STAGE_BYTES + 1024u * (uint32_t)(4 * wave + part);
+                dma16(dA, okc ? va[part] + kbase : OOB, LA + ldst);
+                dma16(dB, okc ? vb[part] + kbase : OOB, LB + ldst);
+            } else {
+                const uint32_t sblk = 2 * (uint32_t)st;  // first k block of the stage
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int ins = 2 * wave + i;
+                    const bool oks = (sblk + (uint32_t)(ins >> 2)) * 32 < R;
+                    const uint32_t ldst = 4u * (q * 512u + 64u * (uint32_t)ins);
+                    dma1(dAs, oks ? vsa[i] + sblk * ldas : OOB, LSA + ldst);
+                    dma1(dBs, oks ? vsb[i] + sblk * ldbs : OOB, LSB + ldst);
+                }
             }
-            rsa = va;
-            rsb = vb;
         };
-        auto store_stage = [&](int buf) {
-            const int q = tid & 7;
+        auto issue = [&](int st) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = (tid >> 3) + 32 * i;
-                *reinterpret_cast<uint4*>(&sm.a[buf][r * BWD_PITCH + 16 * q]) = ra[i];
-                *reinterpret_cast<uint4*>(&sm.b[buf][r * BWD_PITCH + 16 * q]) = rb[i];
-            }
-            sm.sa[buf][tid] = rsa;
-            sm.sb[buf][tid] = rsb;
+            for (int part = 0; part < 5; ++part) issue_part(st, part);
+        };
+        // Fragments of the stage in ring slot Q: lane (row, g) takes logical
+        // chunks g and g+2 of its row (k bytes [16g, +16) and [32+16g, +16):
+        // the MFMA's k order) and the scale of block g.  Part 2i reads the A
+        // rows of group i, part 2i+1 the B rows.
+        auto read_part = [&](uint32_t Q, BwdFrag& f, int part) {
+            const int i = part >> 1;
+            const uint32_t so = ((part & 1) ? fsb : fsa) + Q * 2048u + 128u * i;
+            const uint32_t o = ((part & 1) ? fb : fa) + Q * PIPE_STAGE_BYTES + (uint32_t)(32 * i * PIPE_BK);
+            const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + fr0);
+            const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + fr1);
+            const int sc = *(const __attribute__((address_space(3))) int*)(lds + so);
+            const int8v v = int8v{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+            if (part & 1) { f.b[i] = v; f.sb[i] = sc; } else { f.a[i] = v; f.sa[i] = sc; }
+        };
+        auto read = [&](uint32_t Q, BwdFrag& f) {
+#pragma unroll
+            for (int part = 0; part < 8; ++part) read_part(Q, f, part);
         };
 
         float16v acc[4][4];
@@ -170,60 +243,93 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-        if (nstages > 0) {
-            load_stage(0);
-            store_stage(0);
-        }
-        __syncthreads();
-        for (int s = 0; s < nstages; ++s) {
-            const int buf = s & 1;
-            if (s + 1 < nstages) load_stage(s + 1);
+        auto mma = [&](const BwdFrag& f) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {  // 64-byte MFMA k steps
-                int8v fa[4], fb[4];
-                int sca[4], scb[4];
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ra_ = wm * 128 + 32 * i + lr;
-                    const int rb_ = wn * 128 + 32 * i + lr;
-                    const uint8_t* pa = &sm.a[buf][ra_ * BWD_PITCH + 64 * kk + 16 * g];
-                    const uint8_t* pb = &sm.b[buf][rb_ * BWD_PITCH + 64 * kk + 16 * g];
-                    const uint4 a0 = *reinterpret_cast<const uint4*>(pa);
-                    const uint4 a1 = *reinterpret_cast<const uint4*>(pa + 32);
-                    const uint4 b0 = *reinterpret_cast<const uint4*>(pb);
-                    const uint4 b1 = *reinterpret_cast<const uint4*>(pb + 32);
-                    fa[i] = int8v{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                    fb[i] = int8v{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-                    sca[i] = (int)((sm.sa[buf][ra_] >> (8 * (2 * kk + g))) & 0xFFu);
-                    scb[i] = (int)((sm.sb[buf][rb_] >> (8 * (2 * kk + g))) & 0xFFu);
-                }
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
+                                                                              f.sa[i], 0, f.sb[j]);
+        };
+        // One pipeline step at stage s (fragments in cur): wait until stage
+        // s+1 has landed and every wave holds stage s in registers, then run
+        // the 16 MFMAs of stage s with the refill of ring slot s % 4 (stage
+        // s+4) and the reads of stage s+1 into nxt slotted in between them.
+        // sched_barrier pins the interleave: the memory work issues in the
+        // shadow of the matrix core instead of in front of it.
+        auto step = [&](int s, const BwdFrag& cur, BwdFrag& nxt) {
+            wait_vmcnt<2 * BWD_DMA_PER_STAGE>();
+            wait_lgkmcnt0();
+            block_barrier();
+            const uint32_t qn = (uint32_t)(s + 1) & (PIPE_NST - 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fa[i], fb[j], acc[i][j], 0, 0, 0, sca[i], 0, scb[j]);
+            for (int k = 0; k < 16; ++k) {
+                const int i = k >> 2, j = k & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
+                                                                          cur.sa[i], 0, cur.sb[j]);
+                if (k < 5) issue_part(s + 4, k);
+                else if (k >= 6 && k < 14) read_part(qn, nxt, k - 6);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (s + 1 < nstages) store_stage(buf ^ 1);
-            __syncthreads();
-        }
+        };
 
-        // Epilogue: fp32 accumulators -> f32 or bf16 (round to nearest even).
+        // Prologue: stages 0..3 in flight, stage 0 read into X.
+        issue(0); issue(1); issue(2); issue(3);
+        wait_vmcnt<3 * BWD_DMA_PER_STAGE>();
+        block_barrier();
+        BwdFrag X, Y;
+        read(0, X);
+        int s = 0;
+        for (; s + 1 < nstages; s += 2) {
+            step(s, X, Y);
+            step(s + 1, Y, X);
+        }
+        if (s < nstages) {
+            wait_lgkmcnt0();
+            mma(X);
+        }
+        // drain every DMA of this tile before the ring is reused
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        block_barrier();
+
+        // Epilogue: fp32 accumulators -> f32 or bf16 (round to nearest even)
+        // through buffer stores.  Lane (lr, g) holds column wn*128 + 32j + lr
+        // of rows wm*128 + 32i + 8(v/4) + 4g + v%4; a running row offset
+        // walks the rows and the column tile goes into the immediate offset.
+        // Lanes outside a partial tile get an out-of-range offset and store
+        // nothing.
+        {
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(op.c, 0x7FFFFFFFu);
+            const uint32_t ldcb = (uint32_t)op.ldc * (uint32_t)esz;
+            const int lcol = wn * 128 + lr;
+            int row = wm * 128 + 4 * g;
+            uint32_t vrow = (uint32_t)row * ldcb + (uint32_t)lcol * (uint32_t)esz;
+            const bool whole = (op.rows_a == BWD_BM) & (op.rows_b == BWD_BN);
+            bool okc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = wn * 128 + 32 * j + lr;
-            if (col >= op.rows_b) continue;
+            for (int j = 0; j < 4; ++j) okc[j] = lcol + 32 * j < op.rows_b;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = wm * 128 + 32 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-                    if (row >= op.rows_a) continue;
-                    const int64_t o = (int64_t)row * op.ldc + col;
-                    if (p.out_f32)
-                        reinterpret_cast<float*>(op.c)[o] = acc[i][j][v];
-                    else
-                        reinterpret_cast<uint16_t*>(op.c)[o] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+                for (int vq = 0; vq < 4; ++vq) {
+#pragma unroll
+                    for (int vr = 0; vr < 4; ++vr) {
+                        const bool okr = whole | (row < op.rows_a);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float x = acc[i][j][4 * vq + vr];
+                            const uint32_t vo = (whole | (okr & okc[j])) ? vrow + (uint32_t)(32 * j * esz) : OOB;
+                            if constexpr (OUT_F32)
+                                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rc, (int)vo, 0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(x), rc, (int)vo, 0, 0);
+                        }
+                        row += 1;
+                        vrow += ldcb;
+                    }
+                    row += 4;
+                    vrow += 4 * ldcb;
                 }
             }
         }
@@ -244,12 +350,18 @@ hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s) {
     if (err != hipSuccess) return err;
     static bool attr_set = false;  // idempotent; racing writers set the same value
     if (!attr_set) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8),
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(BwdSmem));
+        if (err != hipSuccess) return err;
+        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(BwdSmem));
         if (err != hipSuccess) return err;
         attr_set = true;
     }
-    hipLaunchKernelGGL(k_gemm_bwd_mxfp8, dim3(grid), dim3(256), sizeof(BwdSmem), s, args);
+    if (args.out_f32)
+        hipLaunchKernelGGL(k_gemm_bwd_mxfp8<true>, dim3(grid), dim3(256), sizeof(BwdSmem), s, args);
+    else
+        hipLaunchKernelGGL(k_gemm_bwd_mxfp8<false>, dim3(grid), dim3(256), sizeof(BwdSmem), s, args);
     return hipGetLastError();
 }
 

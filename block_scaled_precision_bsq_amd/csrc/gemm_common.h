@@ -10,11 +10,14 @@
 //     (by index, or longest-reduction-first when a tile's cost grows with the
 //     expert's token count) and writes per-expert tile prefix sums into the
 //     workspace, zeroing the claim counters;
-//  2. the GEMM runs a persistent grid (one workgroup per CU).  Tiles are dealt
-//     round-robin to the 8 XCDs (tile t belongs to XCD t % 8) and claimed
-//     through one atomic counter per XCD; a workgroup first drains its own
-//     XCD's queue (so tiles sharing an operand panel share that XCD's L2) and
-//     then steals from the others, which balances the tail.
+//  2. the GEMM runs a persistent grid (one workgroup per CU).  The tile list is
+//     cut into chunks of XCD_CHUNK consecutive tiles (one per CU of an XCD);
+//     chunk j belongs to XCD j % 8.  Within an expert, tiles are ordered in
+//     groups of GROUP_M row-tiles x all column-tiles, so one chunk covers a
+//     4 x 8 block of output tiles: 4 A panels and 8 B panels instead of 32 + 1,
+//     which is what one XCD's 4 MB L2 can keep resident per k stage.  Tiles
+//     are claimed through one atomic counter per XCD; a workgroup drains its
+//     own XCD's queue first and then steals from the others.
 // Each output tile is computed by exactly one workgroup in a fixed k order:
 // results do not depend on which workgroup runs it (deterministic, batch
 // invariant; no split-K, no float atomics).
@@ -39,17 +42,32 @@ __host__ __device__ inline int64_t plan_words(int E) { return PLAN_HDR + 2 * (in
 __device__ __forceinline__ const int32_t* plan_start(const int32_t* plan) { return plan + PLAN_HDR; }
 __device__ __forceinline__ const int32_t* plan_order(const int32_t* plan, int E) { return plan + PLAN_HDR + E + 1; }
 
+constexpr int XCD_CHUNK = 32;  // tiles per chunk = CUs per XCD on MI355X
+constexpr int GROUP_M = 4;     // row-tiles per group in the tile order
+
 // Claim the next tile for this workgroup (thread 0 only).  Returns -1 when
 // every queue is drained.  `d` is the number of queues already found empty.
 __device__ __forceinline__ int claim_tile(int32_t* plan, int xcd, int total, int& d) {
     while (d < 8) {
         const int q = (xcd + d) & 7;
         const int c = atomicAdd(&plan[PLAN_CTR + q], 1);
-        const int t = q + 8 * c;
+        const int t = (q + 8 * (c / XCD_CHUNK)) * XCD_CHUNK + (c % XCD_CHUNK);
         if (t < total) return t;
         ++d;
     }
     return -1;
+}
+
+// Grouped order inside one expert: local index -> (row-tile, column-tile).
+// GROUP_M row-tiles are swept together across all `nt` column-tiles.
+__device__ __forceinline__ void grouped_tile(int local, int mt_count, int nt, int& mt, int& ct) {
+    const int per_group = GROUP_M * nt;
+    const int g = local / per_group;
+    const int first = g * GROUP_M;
+    const int rows = min(GROUP_M, mt_count - first);
+    const int r = local - g * per_group;
+    mt = first + r % rows;
+    ct = r / rows;
 }
 
 // Position of tile t in the expert order: last i with tile_start[i] <= t

@@ -100,9 +100,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
         const int pos = find_position(start, p.E, tile);
         const int e = __builtin_amdgcn_readfirstlane(order[pos]);
         const int local = __builtin_amdgcn_readfirstlane(tile - start[pos]);
-        const int mt = local / NT, nt = local % NT;
         const int64_t off0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
         const int64_t off1 = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+        int mt, nt;
+        grouped_tile(local, (int)((off1 - off0 + FWD_BM - 1) / FWD_BM), NT, mt, nt);
         const int64_t m_base = off0 + (int64_t)mt * FWD_BM;
         const int rows_a = (int)min((int64_t)FWD_BM, off1 - m_base);
         const int64_t n_base = (int64_t)nt * FWD_BN;
@@ -128,15 +129,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = (tid >> 2) + 64 * i;
-                ra[i] = buf_load16(rA, (okk && r < rows_a) ? r * kb32 + kb : OOB);
-                rb[i] = buf_load16(rB, (okk && r < rows_b) ? r * kb32 + kb : OOB);
+                ra[i] = buf_load16(rA, (okk & (r < rows_a)) ? r * kb32 + kb : OOB);
+                rb[i] = buf_load16(rB, (okk & (r < rows_b)) ? r * kb32 + kb : OOB);
             }
             const uint32_t ks = (uint32_t)s * FWD_SB;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const bool okj = ks + 4 * j < ks32;
-                rsa[j] = buf_load4(rAs, (okj && tid < rows_a) ? tid * ks32 + ks + 4 * j : OOB);
-                rsb[j] = buf_load4(rBs, (okj && tid < rows_b) ? tid * ks32 + ks + 4 * j : OOB);
+                rsa[j] = buf_load4(rAs, (okj & (tid < rows_a)) ? tid * ks32 + ks + 4 * j : OOB);
+                rsb[j] = buf_load4(rBs, (okj & (tid < rows_b)) ? tid * ks32 + ks + 4 * j : OOB);
             }
         };
         auto store_stage = [&](int buf) {
@@ -166,7 +167,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
         __syncthreads();
         for (int s = 0; s < nstages; ++s) {
             const int buf = s & 1;
-            if (s + 1 < nstages) load_stage(s + 1);
+            // Prefetch the next stage (out-of-range offsets past the last stage
+            // read zeros: the loop body stays one basic block).
+            load_stage(s + 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
             for (int c = 0; c < 2; ++c) {  // 64-element chunks of the stage
                 uint4 qa[4], qb[4];
@@ -198,7 +202,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
                 }
             }
-            if (s + 1 < nstages) store_stage(buf ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+            store_stage(buf ^ 1);
             __syncthreads();
         }
 

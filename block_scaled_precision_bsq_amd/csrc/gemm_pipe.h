@@ -1,0 +1,96 @@
+// LDS staging pipeline shared by the grouped GEMM kernels (gfx950).
+//
+// Operand tiles travel global -> LDS through the buffer-load-to-LDS path
+// ("buffer_load_dwordx4 ... lds"): each wave instruction writes 64 lanes x 16
+// bytes to 1 KB of consecutive LDS starting at M0, with no VGPR staging.  A
+// stage holds 256 rows x 64 bytes per operand; 16 rows fill one instruction,
+// so rows are stored unpadded and the 16-byte chunks of row r are permuted by
+// an XOR swizzle, chunk c living at slot c ^ swz(r).  swz(r) =
+// ((r >> 1) ^ (r >> 2)) & 3 makes the fragment reads -- 16 consecutive rows,
+// one chunk each -- hit 16 distinct 4-bank groups (and 8 rows, 8 groups).
+//
+// Four stages form a ring.  The loads are issued from inline assembly, so the
+// compiler does not see LDS writes in flight and inserts no waits for them;
+// the kernel waits explicitly: s_waitcnt vmcnt(N) for its own DMA groups (the
+// counter retires in order), then s_barrier so every wave's part of a stage is
+// in LDS before anyone reads it, and s_waitcnt lgkmcnt(0) before the barrier
+// that precedes overwriting a ring slot, so all reads of that slot are done.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsq {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int PIPE_ROWS = 256;                  // rows per operand tile
+constexpr int PIPE_BK = 64;                     // bytes per row per stage
+constexpr int PIPE_STAGE_BYTES = PIPE_ROWS * PIPE_BK;
+constexpr int PIPE_NST = 4;                     // ring depth
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Byte offset of logical 16-byte chunk c of row r inside a stage buffer.
+__device__ __forceinline__ int swz_off(int r, int c) { return r * PIPE_BK + 16 * (c ^ swz(r)); }
+
+// Raw buffer descriptor (base, stride 0, num_records, gfx9 data format).
+__device__ __forceinline__ i32x4 make_desc(const void* base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = (int)(uint32_t)a;
+    r.y = (int)((a >> 32) & 0xFFFFu);
+    r.z = 0x7FFFFFFF;
+    r.w = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from desc+voff to LDS lds_base + 16 * lane.  lds_base
+// is wave-uniform (it must reach M0 through an SGPR).
+__device__ __forceinline__ void dma16(i32x4 desc, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
+}
+
+// 4 bytes per lane to lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(i32x4 desc, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
+}
+
+// 1 byte per lane, zero-extended into the dword at lds_base + 4 * lane.
+__device__ __forceinline__ void dma1(i32x4 desc, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_ubyte %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+}  // namespace bsq

@@ -184,14 +184,15 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* 
     uint4* o = reinterpret_cast<uint4*>(codes + row * (int64_t)cols + 32 * b);
     o[0] = r.c0;
     o[1] = r.c1;
-    scale[row * nb + b] = (uint8_t)r.sbyte;
+    scale[(int64_t)b * rows + row] = (uint8_t)r.sbyte;  // block-major scales
 }
 
 // Column-transposing MXFP8 per group: a workgroup owns 128 padded output
 // columns (four 32-blocks of tokens) x 256 channels.  It stages the bf16
 // [128 tokens x 256 channels] tile in LDS with coalesced 16-byte loads, then
 // thread t walks channel t down the tile and writes its 4 blocks as one
-// contiguous 128-byte run of codes[channel][p0 .. p0+128).
+// contiguous 128-byte run of codes[channel][p0 .. p0+128); the block-major
+// scale bytes of neighbouring channels are neighbours in memory.
 constexpr int COLT_TOK = 128;
 constexpr int COLT_CH = 256;
 constexpr int COLT_PITCH = COLT_CH + 8;  // bf16 elements; keeps 16-byte rows aligned
@@ -251,7 +252,6 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
     const int c = c_base + t;
     if (c >= cols) return;
     uint8_t* crow = codes + (int64_t)c * P;
-    uint8_t* srow = scale + (int64_t)c * (P >> 5);
 #pragma unroll 1
     for (int b = 0; b < 4; ++b) {
         const int64_t pc = p0 + 32 * b;
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
         uint4* o = reinterpret_cast<uint4*>(crow + pc);
         o[0] = r.c0;
         o[1] = r.c1;
-        srow[pc >> 5] = (uint8_t)r.sbyte;
+        scale[(pc >> 5) * cols + c] = (uint8_t)r.sbyte;  // block-major: coalesced across channels
     }
 }
 

@@ -40,11 +40,15 @@
  *    bscale [rows][cols/16] u8: E4M3 (OCP E4M3FN) block scale S_b.
  *    rscale [rows] f32: per-row (per-token) decode scale s_row = A / 2688.
  *    Decoded element: e2m1(code) * S_b * s_row.
+ *  MXFP8 scales are stored BLOCK-MAJOR: for a matrix of R rows whose blocks
+ *    of 32 run along its rows, the E8M0 byte (2^(byte-127)) of row r, block b
+ *    is at scale[b * R + r].  (The GEMMs fetch the scales of 256 consecutive
+ *    rows of one block as one contiguous run.)
  *  MXFP8 ROWWISE, rows x cols, cols % 32 == 0:
- *    codes [rows][cols] u8 E4M3; scale [rows][cols/32] u8 E8M0 (2^(byte-127)).
+ *    codes [rows][cols] u8 E4M3; scale [cols/32][rows].
  *  MXFP8 COLWISE_T of an input [rows][cols] with groups `offsets`:
  *    blocks of 32 run DOWN the rows of each group and restart at each group;
- *    the output is transposed: codes [cols][P], scale [cols][P/32] with
+ *    the output is transposed: codes [cols][P], scale [P/32][cols] with
  *    P = bsq_colwise_padded_cols(num_groups, rows) = 32*(num_groups +
  *    ceil(rows/32)).  Group g starts at column c0(g) = 32*(g + offsets[g]/32)
  *    (integer division) and spans 32*ceil(M_g/32) columns; every byte not
@@ -114,10 +118,10 @@ bsq_status bsq_quantize_nvfp4v(const void* x_bf16, int64_t rows, int64_t cols, i
  * sh = clamp(floor(log2 A) - 8, -127, 127), scale byte sh+127, codes
  * sign(x) | E4M3_RNE_sat(x * 2^-sh) (exact power-of-two scaling).
  *   x_bf16 [rows][ld_x] bf16, 16-byte aligned, ld_x % 8 == 0, ld_x >= cols.
- *   BSQ_ROWWISE: cols % 32 == 0; codes [rows][cols], scale [rows][cols/32];
+ *   BSQ_ROWWISE: cols % 32 == 0; codes [rows][cols], scale [cols/32][rows];
  *     offsets may be NULL.
  *   BSQ_COLWISE_T: cols % 8 == 0; offsets required (num_groups >= 1);
- *     codes [cols][P], scale [cols][P/32], P = bsq_colwise_padded_cols(
+ *     codes [cols][P], scale [P/32][cols], P = bsq_colwise_padded_cols(
  *     num_groups, rows); every output byte is written (padding = 0).
  *     Quantizing expert weights W [E][N][K] as rows = E*N with offsets
  *     {0, N, 2N, ...} gives the dgrad operand Wt: codes [K][P_w].
@@ -157,11 +161,12 @@ bsq_status bsq_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_bscale,
  *   BSQ_DGRAD: dx[m][j] = sum_i dy[m][i] * W_e[i][j]   (reduction over n)
  *     dy_codes/dy_scale: MXFP8 ROWWISE of dy [m_total][n];
  *     wt_codes/wt_scale: MXFP8 COLWISE_T of W viewed as [E*n][k] with offsets
- *     {0, n, 2n, ...}: [k][P_w], P_w = bsq_colwise_padded_cols(E, E*n).
+ *     {0, n, 2n, ...}: codes [k][P_w], scale [P_w/32][k],
+ *     P_w = bsq_colwise_padded_cols(E, E*n).
  *     dx [m_total][k] in dx_dtype.
  *   BSQ_WGRAD: dW_e[i][j] = sum_{m in segment e} dy[m][i] * x[m][j]
- *     dyt_*: MXFP8 COLWISE_T of dy with `offsets` ([n][P]);
- *     xt_*:  MXFP8 COLWISE_T of x with `offsets` ([k][P]),
+ *     dyt_*: MXFP8 COLWISE_T of dy with `offsets` (codes [n][P], scale [P/32][n]);
+ *     xt_*:  MXFP8 COLWISE_T of x with `offsets` (codes [k][P], scale [P/32][k]),
  *     P = bsq_colwise_padded_cols(num_experts, m_total).
  *     dw [num_experts][n][k] in dw_dtype; an empty expert gets zeros.
  * Products are formed by the block-scaled MFMA (E8M0 scales applied inside

@@ -67,7 +67,7 @@ def lib():
         L.orc_colwise_padded_cols.argtypes = [I32, I64]; L.orc_colwise_padded_cols.restype = I64
         L.orc_quantize_mxfp8_colwise_t.argtypes = [P, I64, I64, I64, P, I32, P, P]
         L.orc_quantize_mxfp8_colwise_t.restype = None
-        L.orc_dequant_mxfp8.argtypes = [P, P, I64, I64, I64, I64, P]; L.orc_dequant_mxfp8.restype = None
+        L.orc_dequant_mxfp8.argtypes = [P, P, I64, I64, I64, I64, I64, P]; L.orc_dequant_mxfp8.restype = None
         _lib = L
     return _lib
 
@@ -157,13 +157,13 @@ def dequant_nvfp4v(codes, bscale, rscale) -> np.ndarray:
 
 def quantize_mxfp8_rowwise(x_bf16: np.ndarray):
     """MXFP8 with blocks of 32 along each row.  Returns (codes [rows, cols],
-    scale [rows, cols/32])."""
+    scale [cols/32, rows]) -- scales block-major."""
     x = _bf16(x_bf16)
     rows, cols = x.shape
     if cols % 32:
         raise ValueError("cols must be a multiple of 32")
     codes = np.empty((rows, cols), np.uint8)
-    scale = np.empty((rows, cols // 32), np.uint8)
+    scale = np.empty((cols // 32, rows), np.uint8)
     lib().orc_quantize_mxfp8_rowwise(_ptr(x), rows, cols, cols, _ptr(codes), _ptr(scale))
     return codes, scale
 
@@ -180,26 +180,29 @@ def segment_start(g: int, offsets) -> int:
 def quantize_mxfp8_colwise_t(x_bf16: np.ndarray, offsets):
     """MXFP8 with blocks of 32 running down the rows of each segment
     ``[offsets[g], offsets[g+1])``; output transposed and per-segment padded.
-    Returns (codes [cols, P], scale [cols, P/32])."""
+    Returns (codes [cols, P], scale [P/32, cols]) -- scales block-major."""
     x = _bf16(x_bf16)
     rows, cols = x.shape
     off = np.ascontiguousarray(offsets, np.int32)
     G = len(off) - 1
     P = padded_cols(G, rows)
     codes = np.empty((cols, P), np.uint8)
-    scale = np.empty((cols, P // 32), np.uint8)
+    scale = np.empty((P // 32, cols), np.uint8)
     lib().orc_quantize_mxfp8_colwise_t(_ptr(x), rows, cols, cols, _ptr(off), G, _ptr(codes), _ptr(scale))
     return codes, scale
 
 
 def dequant_mxfp8(codes, scale) -> np.ndarray:
-    """Dequantize a matrix whose MXFP8 blocks run along its rows (ROWWISE
-    output, or a COLWISE_T output read as [cols, P])."""
+    """Dequantize a matrix whose MXFP8 blocks run along its rows (a ROWWISE
+    output, or a COLWISE_T output read as [cols, P]); ``scale`` is
+    block-major, [cols/32, rows]."""
     codes = np.ascontiguousarray(codes, np.uint8)
     scale = np.ascontiguousarray(scale, np.uint8)
     rows, cols = codes.shape
+    if scale.shape != (cols // 32, rows):
+        raise ValueError("scale must be block-major [cols/32, rows]")
     out = np.empty((rows, cols), np.float64)
-    lib().orc_dequant_mxfp8(_ptr(codes), _ptr(scale), rows, cols, cols, scale.shape[1], _ptr(out))
+    lib().orc_dequant_mxfp8(_ptr(codes), _ptr(scale), rows, cols, cols, 1, rows, _ptr(out))
     return out
 
 
@@ -255,9 +258,9 @@ def grouped_gemm_dgrad(dy_q, wt_q, offsets, n, rows=None, absolute=False) -> np.
     for e in np.unique(exp_of):
         sel = np.nonzero(exp_of == e)[0]
         r = rows[sel]
-        dy_hat = dequant_mxfp8(dy_q[0][r], dy_q[1][r])
+        dy_hat = dequant_mxfp8(dy_q[0][r], dy_q[1][:, r])
         c0 = segment_start(int(e), woff)
-        wt_hat = dequant_mxfp8(wt_q[0][:, c0:c0 + n], wt_q[1][:, c0 // 32:c0 // 32 + n // 32])
+        wt_hat = dequant_mxfp8(wt_q[0][:, c0:c0 + n], wt_q[1][c0 // 32:c0 // 32 + n // 32, :])
         if absolute:
             dy_hat, wt_hat = np.abs(dy_hat), np.abs(wt_hat)
         out[sel] = dy_hat @ wt_hat.T
@@ -280,8 +283,8 @@ def grouped_gemm_wgrad(dyt_q, xt_q, offsets, experts=None, absolute=False) -> di
         m_e = int(off[e + 1] - off[e])
         c0 = segment_start(int(e), off)
         L = 32 * ((m_e + 31) // 32)
-        dyt = dequant_mxfp8(dyt_q[0][:, c0:c0 + L], dyt_q[1][:, c0 // 32:c0 // 32 + L // 32])
-        xt = dequant_mxfp8(xt_q[0][:, c0:c0 + L], xt_q[1][:, c0 // 32:c0 // 32 + L // 32])
+        dyt = dequant_mxfp8(dyt_q[0][:, c0:c0 + L], dyt_q[1][c0 // 32:c0 // 32 + L // 32, :])
+        xt = dequant_mxfp8(xt_q[0][:, c0:c0 + L], xt_q[1][c0 // 32:c0 // 32 + L // 32, :])
         if absolute:
             dyt, xt = np.abs(dyt), np.abs(xt)
         res[int(e)] = dyt @ xt.T

@@ -38,11 +38,14 @@
  *  MXFP8    per 32-block: A = max|x|; A == 0 -> scale byte 0, codes 0.
  *           Else sh = clamp(floor(log2 A) - 8, -127, 127) (8 = E4M3 emax),
  *           scale byte = sh + 127, code = sign(x) | E4M3(x * 2^-sh).
+ *           Scales are stored block-major: the byte of (row r, block b) of an
+ *           R-row matrix is at b * R + r.
  *  COLWISE_T  the MXFP8 blocks run down the rows (tokens) of each segment
  *           [off[g], off[g+1]) and restart at each segment; the output is
- *           transposed, [cols][P] with P = 32*(G + ceil(rows/32)); segment g
- *           starts at column c0[g] = 32*(g + floor(off[g]/32)); every other
- *           byte (padding, gaps) is 0.
+ *           transposed, codes [cols][P] with P = 32*(G + ceil(rows/32)),
+ *           scales [P/32][cols] (block-major); segment g starts at column
+ *           c0[g] = 32*(g + floor(off[g]/32)); every other byte (padding,
+ *           gaps) is 0.
  */
 #include <math.h>
 #include <stdint.h>
@@ -209,6 +212,7 @@ static int mx_shift(float A) {
 }
 
 static void mx_block(const float* v, int n, uint8_t* code_out, int64_t code_stride, uint8_t* scale_out) {
+    /* one block of n <= 32 values: codes at code_out[i * code_stride], E8M0 at *scale_out */
     float A = 0.0f;
     for (int i = 0; i < n; ++i) A = fmaxf(A, fabsf(v[i]));
     if (A == 0.0f) {
@@ -232,7 +236,7 @@ ORC_API void orc_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows, int64_t
         float v[32];
         for (int64_t b = 0; b < nb; ++b) {
             for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(x[r * ldx + 32 * b + i]);
-            mx_block(v, 32, codes + r * cols + 32 * b, 1, scale + r * nb + b);
+            mx_block(v, 32, codes + r * cols + 32 * b, 1, scale + b * rows + r);
         }
     }
 }
@@ -257,19 +261,19 @@ ORC_API void orc_quantize_mxfp8_colwise_t(const uint16_t* x, int64_t rows, int64
                 const int64_t mb = m0 + 32 * j;
                 const int n = (int)((m1 - mb) < 32 ? (m1 - mb) : 32);
                 for (int i = 0; i < n; ++i) v[i] = bf16_to_f32(x[(mb + i) * ldx + c]);
-                mx_block(v, n, codes + c * P + c0 + 32 * j, 1, scale + c * (P / 32) + c0 / 32 + j);
+                mx_block(v, n, codes + c * P + c0 + 32 * j, 1, scale + (c0 / 32 + j) * cols + c);
             }
         }
     }
 }
 
-/* Dequantize an MXFP8 matrix in "blocks along the contiguous dimension"
- * layout: element (r, c) = E4M3(codes[r*ld_codes + c]) * E8M0(scale[r*ld_scale + c/32]). */
+/* Dequantize an MXFP8 matrix whose blocks run along its rows: element (r, c) =
+ * E4M3(codes[r*ld_codes + c]) * E8M0(scale[r*s_row + (c/32)*s_blk]). */
 ORC_API void orc_dequant_mxfp8(const uint8_t* codes, const uint8_t* scale, int64_t rows, int64_t cols,
-                               int64_t ld_codes, int64_t ld_scale, double* out) {
+                               int64_t ld_codes, int64_t s_row, int64_t s_blk, double* out) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c)
             out[r * cols + c] = orc_e4m3_value(codes[r * ld_codes + c]) *
-                                orc_e8m0_value(scale[r * ld_scale + c / 32]);
+                                orc_e8m0_value(scale[r * s_row + (c / 32) * s_blk]);
 }

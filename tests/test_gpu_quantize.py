@@ -215,5 +215,5 @@ def test_mxfp8_colwise_t_full_size_sampled(orc, bsq_gpu):
     x_ch = _np(dy[:, torch.from_numpy(ch).cuda()].contiguous().view(torch.int16)).view(np.uint16)
     rc, rs = orc.quantize_mxfp8_colwise_t(np.ascontiguousarray(x_ch), off)
     gcn = _np(gc[torch.from_numpy(ch).cuda()])
-    gsn = _np(gs[torch.from_numpy(ch).cuda()])
+    gsn = _np(gs[:, torch.from_numpy(ch).cuda()])
     assert np.array_equal(rc, gcn) and np.array_equal(rs, gsn)

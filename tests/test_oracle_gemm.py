@@ -130,6 +130,7 @@ def _mx_exact_tn(ac, asc, bc, bsc):
     A = t[ac].reshape(ac.shape[0], -1, 32)
     B = t[bc].reshape(bc.shape[0], -1, 32)
     part = np.einsum("ibk,jbk->ijb", A, B)  # int64, exact per block
+    asc, bsc = asc.T, bsc.T  # block-major scales -> [rows, blocks]
     sh = (asc.astype(np.int64) - 127)[:, None, :] + (bsc.astype(np.int64) - 127)[None, :, :]
     return (part.astype(np.float64) * np.exp2(sh - 18)).sum(-1), (np.abs(part).astype(np.float64) *
                                                                 np.exp2(sh - 18)).sum(-1)
@@ -152,8 +153,8 @@ def test_dgrad_matches_exact_blocks(orc):
         if m0 == m1:
             continue
         c0 = 32 * (e + woff[e] // 32)
-        ref, absum = _mx_exact_tn(dy_q[0][m0:m1], dy_q[1][m0:m1], wt_q[0][:, c0:c0 + n],
-                                  wt_q[1][:, c0 // 32:(c0 + n) // 32])
+        ref, absum = _mx_exact_tn(dy_q[0][m0:m1], dy_q[1][:, m0:m1], wt_q[0][:, c0:c0 + n],
+                                  wt_q[1][c0 // 32:(c0 + n) // 32, :])
         assert np.all(np.abs(dx[m0:m1] - ref) <= 1e-12 * absum + 1e-300)
 
 
@@ -175,13 +176,13 @@ def test_wgrad_matches_exact_blocks_and_outer_products(orc):
             continue
         c0 = 32 * (e + m0 // 32)
         L = 32 * ((m1 - m0 + 31) // 32)
-        ref, absum = _mx_exact_tn(dyt[0][:, c0:c0 + L], dyt[1][:, c0 // 32:(c0 + L) // 32],
-                                  xt[0][:, c0:c0 + L], xt[1][:, c0 // 32:(c0 + L) // 32])
+        ref, absum = _mx_exact_tn(dyt[0][:, c0:c0 + L], dyt[1][c0 // 32:(c0 + L) // 32, :],
+                                  xt[0][:, c0:c0 + L], xt[1][c0 // 32:(c0 + L) // 32, :])
         assert np.all(np.abs(dw[e] - ref) <= 1e-12 * absum + 1e-300)
         # independent structure: sum of per-token outer products of the
         # dequantized token vectors
-        dyh = orc.dequant_mxfp8(dyt[0][:, c0:c0 + L], dyt[1][:, c0 // 32:(c0 + L) // 32])
-        xh = orc.dequant_mxfp8(xt[0][:, c0:c0 + L], xt[1][:, c0 // 32:(c0 + L) // 32])
+        dyh = orc.dequant_mxfp8(dyt[0][:, c0:c0 + L], dyt[1][c0 // 32:(c0 + L) // 32, :])
+        xh = orc.dequant_mxfp8(xt[0][:, c0:c0 + L], xt[1][c0 // 32:(c0 + L) // 32, :])
         acc = np.zeros((n, k))
         for j in range(m1 - m0):
             acc += np.outer(dyh[:, j], xh[:, j])

@@ -174,7 +174,7 @@ def test_mxfp8_worked_blocks(orc):
         for k, v in vals.items():
             x[0, k] = v
         c, s = orc.quantize_mxfp8_rowwise(bf16(x))
-        assert s[0, 0] == sbyte, vals
+        assert s.shape == (1, 1) and s[0, 0] == sbyte, vals
         for k, v in codes.items():
             assert c[0, k] == v, (vals, k)
 
@@ -192,10 +192,10 @@ def test_mxfp8_rowwise_vs_frexp_and_torch(orc):
             blk = xf[r, b]
             A = np.abs(blk).max()
             if A == 0:
-                assert scale[r, b] == 0 and not codes[r, 32 * b:32 * b + 32].any()
+                assert scale[b, r] == 0 and not codes[r, 32 * b:32 * b + 32].any()
                 continue
             sh = min(max(math.frexp(A)[1] - 1 - 8, -127), 127)
-            assert scale[r, b] == sh + 127
+            assert scale[b, r] == sh + 127
             scaled = np.clip(blk * 2.0 ** -sh, -448, 448).astype(np.float32)
             ref = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
             assert np.array_equal(codes[r, 32 * b:32 * b + 32], ref), (r, b)
@@ -211,7 +211,7 @@ def test_mxfp8_symmetries_and_bound(orc):
     c2, s2 = orc.quantize_mxfp8_rowwise(bf16(xf * np.float32(2.0 ** 9)))
     assert np.array_equal(c2, c0) and np.array_equal(s2.astype(int), s0.astype(int) + 9)
     xhat = orc.dequant_mxfp8(c0, s0)
-    sh = np.repeat(s0.astype(np.float64) - 127, 32, axis=1)
+    sh = np.repeat(s0.T.astype(np.float64) - 127, 32, axis=1)
     a = np.abs(xf.astype(np.float64))
     bound = np.maximum.reduce([2.0 ** -4 * a, 2.0 ** (sh - 10), a - 448 * 2.0 ** sh])
     assert np.all(np.abs(a * np.sign(xf) - xhat) <= bound)
@@ -236,7 +236,7 @@ def test_mxfp8_colwise_t_matches_rowwise_on_transposed_segments(orc):
     x = make_quantize_input(rng, rows, cols)
     codes, scale = orc.quantize_mxfp8_colwise_t(x, off)
     P = 32 * (G + (rows + 31) // 32)
-    assert codes.shape == (cols, P) and scale.shape == (cols, P // 32)
+    assert codes.shape == (cols, P) and scale.shape == (P // 32, cols)
     covered = np.zeros(P, bool)
     for g in range(G):
         m0, m1 = int(off[g]), int(off[g + 1])
@@ -248,7 +248,7 @@ def test_mxfp8_colwise_t_matches_rowwise_on_transposed_segments(orc):
         seg[:, :m1 - m0] = x[m0:m1].T
         rc, rs = orc.quantize_mxfp8_rowwise(seg)
         assert np.array_equal(codes[:, c0:c0 + L], rc)
-        assert np.array_equal(scale[:, c0 // 32:(c0 + L) // 32], rs)
+        assert np.array_equal(scale[c0 // 32:(c0 + L) // 32, :], rs)
     assert not codes[:, ~covered].any()
-    assert not scale[:, ~covered[::32]].any()
+    assert not scale[~covered[::32], :].any()
     assert covered.sum() <= P
