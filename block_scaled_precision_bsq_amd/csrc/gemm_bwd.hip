@@ -22,11 +22,14 @@
 // g: memory order is the hardware k order.
 //
 // Tiling: 256 x 256 outputs per workgroup (4 waves, 2 x 2, 128 x 128 each:
-// 4 x 4 MFMA tiles, fp32 accumulators in AGPRs).  k runs in 64-byte stages
-// (one MFMA k step) through a 4-deep LDS ring filled by buffer-to-LDS DMA
-// (gemm_pipe.h): three stages are in flight while one is multiplied, and the
-// fragments of stage s+1 are read from LDS into a second register set while
-// the MFMAs of stage s run.
+// 4 x 4 MFMA tiles, fp32 accumulators in AGPRs).  k runs in 128-byte
+// super-stages (two MFMA k steps) through a 2-slot LDS ring filled by
+// buffer-to-LDS DMA (gemm_pipe.h).  One DMA instruction moves 8 rows x 128
+// bytes, i.e. whole 128-byte cache lines: fetching half lines (64-byte rows)
+// caps the L2-to-CU stream near half of what full lines reach.  Fragments are
+// double-buffered in registers per 64-byte k step: the MFMAs of step t run
+// while step t+1 is read from LDS, and a ring slot is refilled as soon as both
+// of its steps sit in registers.
 #include "device_common.h"
 #include "gemm_common.h"
 #include "gemm_pipe.h"
@@ -38,14 +41,22 @@ namespace bsq {
 
 constexpr int BWD_BM = 256;
 constexpr int BWD_BN = 256;
-constexpr int BWD_DMA_PER_STAGE = 12;  // DMA instructions per wave per stage
+constexpr int SS_BK = 128;                       // bytes of k per row per super-stage
+constexpr int SS_TILE = PIPE_ROWS * SS_BK;       // one operand's super-stage (32 KB)
+constexpr int SS_DMA = 24;                       // DMA instructions per wave per super-stage
 
 struct BwdSmem {
-    uint8_t a[PIPE_NST][PIPE_STAGE_BYTES];
-    uint8_t b[PIPE_NST][PIPE_STAGE_BYTES];
-    uint32_t sa[PIPE_NST][PIPE_ROWS * 2];  // E8M0 byte of (block, row) in dword block*256 + row
-    uint32_t sb[PIPE_NST][PIPE_ROWS * 2];
+    uint8_t a[2][SS_TILE];
+    uint8_t b[2][SS_TILE];
+    uint32_t sa[2][4 * PIPE_ROWS];  // E8M0 byte of (k block, row) in dword block*256 + row
+    uint32_t sb[2][4 * PIPE_ROWS];
 };
+
+// 128-byte rows hold 8 chunks of 16 bytes; chunk c of row r lives in slot
+// c ^ swz8(r).  A 16-lane quarter of a fragment read covers 16 consecutive
+// rows at one chunk: rows of equal parity share 8-chunk halves of the 64 LDS
+// banks and swz8 = (r >> 1) & 7 spreads them over all 8 slots.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 // One output tile of C[i][j] = sum_r A[i][r] B[j][r].
 struct TileOps {
@@ -59,8 +70,6 @@ struct BwdFrag {
     int8v a[4], b[4];
     int sa[4], sb[4];
 };
-
-template <int V> using IC = std::integral_constant<int, V>;
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
@@ -81,7 +90,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     const int32_t* order = plan_order(p.plan, p.E);
     int dq = 0;
 
-    // 32-bit LDS byte addresses of the ring buffers
+    // 32-bit LDS byte addresses of the ring (DMA targets go through M0)
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
     const uint32_t LA = lds0 + offsetof(BwdSmem, a), LB = lds0 + offsetof(BwdSmem, b);
     const uint32_t LSA = lds0 + offsetof(BwdSmem, sa), LSB = lds0 + offsetof(BwdSmem, sb);
@@ -89,19 +98,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     const __attribute__((address_space(3))) uint8_t* lds =
         (const __attribute__((address_space(3))) uint8_t*)(smem_raw);
 
-    // DMA lane geometry (tile-invariant): instruction i of this wave covers
-    // rows 16 * (4 * wave + i) + lane / 4; the lane fetches logical chunk
-    // (lane & 3) ^ swz(row) of its row into slot lane & 3.  swz(row) depends
-    // only on bits 1..3 of the row, i.e. on lane / 4.
-    const int drow0 = 64 * wave + (lane >> 2);
-    const uint32_t dchunk = (uint32_t)((lane & 3) ^ swz(lane >> 2));
-    const bool dlow = dchunk < 2;  // chunk lies in the first 32-byte k block
-    // Fragment read geometry: lane (lr, g) reads chunks g and g + 2 of row
-    // lr of each 32-row group; swz(row) = swz(lr) for every such row.
-    const uint32_t fr0 = (uint32_t)(lr * PIPE_BK + 16 * (g ^ swz(lr)));
-    const uint32_t fr1 = fr0 ^ 32u;  // chunk g + 2
-    const uint32_t fa = offsetof(BwdSmem, a) + (uint32_t)(wm * 128 * PIPE_BK);
-    const uint32_t fb = offsetof(BwdSmem, b) + (uint32_t)(wn * 128 * PIPE_BK);
+    // DMA lane geometry: code instruction i (0..7) of this wave covers rows
+    // 64 * wave + 8 * i + lane / 8; the lane fetches logical chunk
+    // (lane & 7) ^ swz8(row) into slot lane & 7.  swz8(row) depends on lane / 8
+    // and on the parity of i.
+    const int drow0 = 64 * wave + (lane >> 3);
+    const uint32_t dch0 = (uint32_t)((lane & 7) ^ swz8(lane >> 3));        // even i
+    const uint32_t dch1 = (uint32_t)((lane & 7) ^ swz8(8 + (lane >> 3)));  // odd i
+    // Fragment read geometry: lane (lr, g) of k step h reads chunks 4h + g and
+    // 4h + g + 2 of row lr of each 32-row group; swz8(row) = swz8(lr), and
+    // (4h + g + 2d) ^ swz8 = (g ^ swz8) ^ (4h + 2d).
+    const uint32_t fr = (uint32_t)(lr * SS_BK + 16 * (g ^ swz8(lr)));
+    const uint32_t fa = offsetof(BwdSmem, a) + (uint32_t)(wm * 128 * SS_BK);
+    const uint32_t fb = offsetof(BwdSmem, b) + (uint32_t)(wn * 128 * SS_BK);
     const uint32_t fsa = offsetof(BwdSmem, sa) + 4u * (uint32_t)(256 * g + wm * 128 + lr);
     const uint32_t fsb = offsetof(BwdSmem, sb) + 4u * (uint32_t)(256 * g + wn * 128 + lr);
 
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         op.ldc = uniform_i64(op.ldc); op.R = uniform_i64(op.R);
         op.rows_a = __builtin_amdgcn_readfirstlane(op.rows_a);
         op.rows_b = __builtin_amdgcn_readfirstlane(op.rows_b);
-        const int nstages = (int)((op.R + PIPE_BK - 1) / PIPE_BK);
+        const int nsteps = (int)((op.R + 63) / 64);  // 64-byte MFMA k steps
 
         const i32x4 dA = make_desc(op.a), dB = make_desc(op.b);
         const i32x4 dAs = make_desc(op.as), dBs = make_desc(op.bs);
@@ -164,75 +173,70 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         const uint32_t ldas = (uint32_t)op.ldas, ldbs = (uint32_t)op.ldbs;
         const uint32_t R = (uint32_t)op.R;
 
-        // Per-tile lane offsets at k = 0; rows past the tile read as zero.
-        uint32_t va[4], vb[4];
+        // Per-tile lane offsets at k = 0 (row part; the chunk is added per
+        // instruction); rows past the tile read as zero.
+        const uint32_t vra = (uint32_t)drow0 * lda, vrb = (uint32_t)drow0 * ldb;
+        // scales: instruction i (of 4) covers k block (4 * wave + i) >> 2 of
+        // the super-stage, rows 64 * ((4 * wave + i) & 3) + lane
+        uint32_t vsa[4], vsb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = drow0 + 16 * i;
-            va[i] = row < op.rows_a ? (uint32_t)row * lda + 16 * dchunk : OOB;
-            vb[i] = row < op.rows_b ? (uint32_t)row * ldb + 16 * dchunk : OOB;
-        }
-        // scales: instruction i (of 2) covers k block (2 * wave + i) >> 2 of
-        // the stage, rows 64 * ((2 * wave + i) & 3) + lane
-        uint32_t vsa[2], vsb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int ins = 2 * wave + i;
+            const int ins = 4 * wave + i;
             const int row = 64 * (ins & 3) + lane;
             const uint32_t kb = (uint32_t)(ins >> 2);
             vsa[i] = row < op.rows_a ? kb * ldas + row : OOB;
             vsb[i] = row < op.rows_b ? kb * ldbs + row : OOB;
         }
 
-        // DMA of stage st into ring slot st % 4: 12 instructions per wave,
-        // issued in 5 parts (part i < 4: A and B rows of instruction i; part
-        // 4: the four scale instructions).  Stages past the end land as
-        // zeros, which keeps the per-stage instruction count, and so the
-        // vmcnt bookkeeping, uniform.  R is a multiple of 32: a stage is
-        // either whole, half (its first k block only) or past the end.
-        auto issue_part = [&](int st, int part) {
-            const uint32_t q = (uint32_t)st & (PIPE_NST - 1);
-            const uint32_t kbase = (uint32_t)st * PIPE_BK;
-            if (part < 4) {
-                const bool full = kbase + PIPE_BK <= R;
-                const bool half = kbase + 32 == R;
-                const bool okc = full | (half & dlow);
-                const uint32_t ldst = q * PIPE_STAGE_BYTES + 1024u * (uint32_t)(4 * wave + part);
-                dma16(dA, okc ? va[part] + kbase : OOB, LA + ldst);
-                dma16(dB, okc ? vb[part] + kbase : OOB, LB + ldst);
+        // DMA of super-stage S into ring slot S % 2 (24 instructions per
+        // wave), in 12 parts of 2 so they can sit between MFMAs: parts 0..7
+        // move code rows (A and B of instruction i), parts 8..11 scale blocks.
+        // A 16-byte chunk or a 32-element scale block past R reads as zero.
+        auto issue_part = [&](int S, int part) {
+            const uint32_t q = (uint32_t)S & 1;
+            const uint32_t kbase = (uint32_t)S * SS_BK;
+            if (part < 8) {
+                const int i = part;
+                const int row = drow0 + 8 * i;
+                const uint32_t ch = (i & 1) ? dch1 : dch0;
+                const bool okk = kbase + 16 * ch < R;
+                const uint32_t ko = kbase + 16 * ch;
+                const uint32_t ldst = q * SS_TILE + 1024u * (uint32_t)(8 * wave + i);
+                dma16(dA, (okk & (row < op.rows_a)) ? vra + (uint32_t)(8 * i) * lda + ko : OOB, LA + ldst);
+                dma16(dB, (okk & (row < op.rows_b)) ? vrb + (uint32_t)(8 * i) * ldb + ko : OOB, LB + ldst);
             } else {
-                const uint32_t sblk = 2 * (uint32_t)st;  // first k block of the stage
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int ins = 2 * wave + i;
-                    const bool oks = (sblk + (uint32_t)(ins >> 2)) * 32 < R;
-                    const uint32_t ldst = 4u * (q * 512u + 64u * (uint32_t)ins);
-                    dma1(dAs, oks ? vsa[i] + sblk * ldas : OOB, LSA + ldst);
-                    dma1(dBs, oks ? vsb[i] + sblk * ldbs : OOB, LSB + ldst);
-                }
+                const int i = part - 8;
+                const int ins = 4 * wave + i;
+                const uint32_t blk = 4 * (uint32_t)S + (uint32_t)(ins >> 2);
+                const bool oks = blk * 32 < R;
+                const uint32_t sblk = 4 * (uint32_t)S;
+                const uint32_t ldst = 4u * (q * 1024u + 64u * (uint32_t)ins);
+                dma1(dAs, oks ? vsa[i] + sblk * ldas : OOB, LSA + ldst);
+                dma1(dBs, oks ? vsb[i] + sblk * ldbs : OOB, LSB + ldst);
             }
         };
-        auto issue = [&](int st) {
+        auto issue = [&](int S) {
 #pragma unroll
-            for (int part = 0; part < 5; ++part) issue_part(st, part);
+            for (int part = 0; part < 12; ++part) issue_part(S, part);
         };
-        // Fragments of the stage in ring slot Q: lane (row, g) takes logical
-        // chunks g and g+2 of its row (k bytes [16g, +16) and [32+16g, +16):
-        // the MFMA's k order) and the scale of block g.  Part 2i reads the A
+        // Fragments of k step t (ring slot (t / 2) % 2, half h = t % 2): lane
+        // (row, g) takes logical chunks 4h + g and 4h + g + 2 of its row (the
+        // MFMA's k order) and the scale of block 2h + g.  Part 2i reads the A
         // rows of group i, part 2i+1 the B rows.
-        auto read_part = [&](uint32_t Q, BwdFrag& f, int part) {
+        auto read_part = [&](int t, BwdFrag& f, int part) {
+            const uint32_t q = ((uint32_t)t >> 1) & 1, h = (uint32_t)t & 1;
             const int i = part >> 1;
-            const uint32_t so = ((part & 1) ? fsb : fsa) + Q * 2048u + 128u * i;
-            const uint32_t o = ((part & 1) ? fb : fa) + Q * PIPE_STAGE_BYTES + (uint32_t)(32 * i * PIPE_BK);
-            const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + fr0);
-            const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + fr1);
+            const uint32_t so = ((part & 1) ? fsb : fsa) + q * 4096u + h * 2048u + 128u * i;
+            const uint32_t o = ((part & 1) ? fb : fa) + q * SS_TILE + (uint32_t)(32 * i * SS_BK);
+            const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + (fr ^ (64u * h)));
+            const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + (fr ^ (64u * h + 32u)));
             const int sc = *(const __attribute__((address_space(3))) int*)(lds + so);
             const int8v v = int8v{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
             if (part & 1) { f.b[i] = v; f.sb[i] = sc; } else { f.a[i] = v; f.sa[i] = sc; }
         };
-        auto read = [&](uint32_t Q, BwdFrag& f) {
+        auto read = [&](int t, BwdFrag& f) {
 #pragma unroll
-            for (int part = 0; part < 8; ++part) read_part(Q, f, part);
+            for (int part = 0; part < 8; ++part) read_part(t, f, part);
         };
 
         float16v acc[4][4];
@@ -251,40 +255,51 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
                                                                               f.sa[i], 0, f.sb[j]);
         };
-        // One pipeline step at stage s (fragments in cur): wait until stage
-        // s+1 has landed and every wave holds stage s in registers, then run
-        // the 16 MFMAs of stage s with the refill of ring slot s % 4 (stage
-        // s+4) and the reads of stage s+1 into nxt slotted in between them.
-        // sched_barrier pins the interleave: the memory work issues in the
-        // shadow of the matrix core instead of in front of it.
-        auto step = [&](int s, const BwdFrag& cur, BwdFrag& nxt) {
-            wait_vmcnt<2 * BWD_DMA_PER_STAGE>();
+        // k step t (fragments in cur) with t even: both halves of its
+        // super-stage are in LDS; the MFMAs of t run with the reads of t+1.
+        auto step_even = [&](int t, const BwdFrag& cur, BwdFrag& nxt) {
             wait_lgkmcnt0();
-            block_barrier();
-            const uint32_t qn = (uint32_t)(s + 1) & (PIPE_NST - 1);
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const int i = k >> 2, j = k & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
                                                                           cur.sa[i], 0, cur.sb[j]);
-                if (k < 5) issue_part(s + 4, k);
-                else if (k >= 6 && k < 14) read_part(qn, nxt, k - 6);
+                if (k >= 2 && k < 10) read_part(t + 1, nxt, k - 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // k step t odd: wait until super-stage t/2 + 1 has landed (the only
+        // DMA in flight) and every wave holds both halves of super-stage t/2
+        // in registers, then refill its slot with super-stage t/2 + 2 while
+        // the MFMAs of t run, and read t+1.
+        auto step_odd = [&](int t, const BwdFrag& cur, BwdFrag& nxt) {
+            wait_vmcnt<0>();
+            wait_lgkmcnt0();
+            block_barrier();
+            const int S = (t >> 1) + 2;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int i = k >> 2, j = k & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
+                                                                          cur.sa[i], 0, cur.sb[j]);
+                if (k < 12) issue_part(S, k);
+                if (k >= 4 && k < 12) read_part(t + 1, nxt, k - 4);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
 
-        // Prologue: stages 0..3 in flight, stage 0 read into X.
-        issue(0); issue(1); issue(2); issue(3);
-        wait_vmcnt<3 * BWD_DMA_PER_STAGE>();
+        // Prologue: super-stages 0 and 1 in flight, k step 0 read into X.
+        issue(0); issue(1);
+        wait_vmcnt<SS_DMA>();
         block_barrier();
         BwdFrag X, Y;
         read(0, X);
-        int s = 0;
-        for (; s + 1 < nstages; s += 2) {
-            step(s, X, Y);
-            step(s + 1, Y, X);
+        int t = 0;
+        for (; t + 1 < nsteps; t += 2) {
+            step_even(t, X, Y);
+            step_odd(t + 1, Y, X);
         }
-        if (s < nstages) {
+        if (t < nsteps) {
             wait_lgkmcnt0();
             mma(X);
         }
