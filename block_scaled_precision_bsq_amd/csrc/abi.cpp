@@ -109,6 +109,8 @@ bsq_status bsq_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t cols, in
     if (rows > 0 && (!x_bf16 || ld_x < cols)) return BSQ_ERR_INVALID_ARG;
     if (cols % 8 || ld_x % 8 || !aligned(x_bf16, 16) || !aligned(codes, 16)) return BSQ_ERR_UNSUPPORTED;
     if (num_groups > (1 << 30)) return BSQ_ERR_UNSUPPORTED;
+    // per-tile load offsets are 32-bit: 128 token rows of ld_x bf16 elements
+    if (258 * ld_x >= kMaxBufferOffset) return BSQ_ERR_UNSUPPORTED;
     const int64_t P = bsq_colwise_padded_cols(num_groups, rows);
     return from_hip(bsq::launch_quantize_mxfp8_colwise_t(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x,
                                                          offsets, num_groups, P, codes, scale, stream));

@@ -308,44 +308,66 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         wait_lgkmcnt0();
         block_barrier();
 
-        // Epilogue: fp32 accumulators -> f32 or bf16 (round to nearest even)
-        // through buffer stores.  Lane (lr, g) holds column wn*128 + 32j + lr
-        // of rows wm*128 + 32i + 8(v/4) + 4g + v%4; a running row offset
-        // walks the rows and the column tile goes into the immediate offset.
-        // Lanes outside a partial tile get an out-of-range offset and store
-        // nothing.
+        // Epilogue: the fp32 tile goes through the (now idle) LDS ring in two
+        // passes of 128 rows (each wave contributes its row groups i = 2p and
+        // 2p+1), then leaves as whole rows in 16-byte stores: f32 as is, bf16
+        // rounded to nearest even.  Lane (lr, g) holds column wn*128 + 32j + lr
+        // of rows wm*128 + 32i + 8(v/4) + 4g + v%4.  The staging pitch of 1056
+        // bytes puts the two lane halves (rows 4 apart) on disjoint banks.
+        // Stores outside a partial tile get an out-of-range offset.
         {
+            constexpr uint32_t EP = 1056;  // bytes per staged row (256 f32 + 32)
             const __amdgpu_buffer_rsrc_t rc = make_rsrc(op.c, 0x7FFFFFFFu);
             const uint32_t ldcb = (uint32_t)op.ldc * (uint32_t)esz;
-            const int lcol = wn * 128 + lr;
-            int row = wm * 128 + 4 * g;
-            uint32_t vrow = (uint32_t)row * ldcb + (uint32_t)lcol * (uint32_t)esz;
-            const bool whole = (op.rows_a == BWD_BM) & (op.rows_b == BWD_BN);
-            bool okc[4];
+            __attribute__((address_space(3))) uint8_t* st = (__attribute__((address_space(3))) uint8_t*)(smem_raw);
+            const uint32_t wbase = (uint32_t)(wm * 64 + 4 * g) * EP + (uint32_t)(wn * 128 + lr) * 4u;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) okc[j] = lcol + 32 * j < op.rows_b;
+            for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int i = 2 * pass + ii;
 #pragma unroll
-                for (int vq = 0; vq < 4; ++vq) {
+                    for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int vr = 0; vr < 4; ++vr) {
-                        const bool okr = whole | (row < op.rows_a);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float x = acc[i][j][4 * vq + vr];
-                            const uint32_t vo = (whole | (okr & okc[j])) ? vrow + (uint32_t)(32 * j * esz) : OOB;
-                            if constexpr (OUT_F32)
-                                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), rc, (int)vo, 0, 0);
-                            else
-                                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(x), rc, (int)vo, 0, 0);
+                        for (int v = 0; v < 16; ++v) {
+                            const uint32_t o = wbase + (uint32_t)(32 * ii + 8 * (v >> 2) + (v & 3)) * EP + 128u * j;
+                            *(__attribute__((address_space(3))) float*)(st + o) = acc[i][j][v];
                         }
-                        row += 1;
-                        vrow += ldcb;
-                    }
-                    row += 4;
-                    vrow += 4 * ldcb;
                 }
+                wait_lgkmcnt0();
+                block_barrier();
+                // staged row r (0..127) is tile row (r / 64) * 128 + 64 * pass + r % 64
+                if constexpr (OUT_F32) {
+#pragma unroll 4
+                    for (int it = 0; it < 32; ++it) {
+                        const int c = it * 256 + tid;          // 64 chunks of 16 bytes per row
+                        const int r = c >> 6, cc = c & 63;
+                        const int row = (r >> 6) * 128 + 64 * pass + (r & 63);
+                        const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 16u * cc);
+                        const bool ok = (row < op.rows_a) & (4 * cc < op.rows_b);
+                        __builtin_amdgcn_raw_buffer_store_b128(x, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0, 0);
+                    }
+                } else {
+#pragma unroll 4
+                    for (int it = 0; it < 16; ++it) {
+                        const int c = it * 256 + tid;          // 32 chunks of 8 bf16 per row
+                        const int r = c >> 5, cc = c & 31;
+                        const int row = (r >> 6) * 128 + 64 * pass + (r & 63);
+                        const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 32u * cc);
+                        const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 32u * cc + 16u);
+                        u32x4 y;
+                        y[0] = f32_to_bf16_rne(__uint_as_float(x0[0])) | (f32_to_bf16_rne(__uint_as_float(x0[1])) << 16);
+                        y[1] = f32_to_bf16_rne(__uint_as_float(x0[2])) | (f32_to_bf16_rne(__uint_as_float(x0[3])) << 16);
+                        y[2] = f32_to_bf16_rne(__uint_as_float(x1[0])) | (f32_to_bf16_rne(__uint_as_float(x1[1])) << 16);
+                        y[3] = f32_to_bf16_rne(__uint_as_float(x1[2])) | (f32_to_bf16_rne(__uint_as_float(x1[3])) << 16);
+                        const bool ok = (row < op.rows_a) & (8 * cc < op.rows_b);
+                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0, 0);
+                    }
+                }
+                // every wave's reads of this pass are done before the next
+                // pass (or the next tile's DMA) overwrites the staging area
+                wait_lgkmcnt0();
+                block_barrier();
             }
         }
     }

@@ -16,6 +16,7 @@
 // This file is compiled with -ffp-contract=off: every float operation below
 // is a single IEEE operation in round-to-nearest-even with denormals kept.
 #include "device_common.h"
+#include "gemm_pipe.h"
 
 namespace bsq {
 
@@ -187,88 +188,130 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* 
     scale[(int64_t)b * rows + row] = (uint8_t)r.sbyte;  // block-major scales
 }
 
-// Column-transposing MXFP8 per group: a workgroup owns 128 padded output
-// columns (four 32-blocks of tokens) x 256 channels.  It stages the bf16
-// [128 tokens x 256 channels] tile in LDS with coalesced 16-byte loads, then
-// thread t walks channel t down the tile and writes its 4 blocks as one
-// contiguous 128-byte run of codes[channel][p0 .. p0+128); the block-major
-// scale bytes of neighbouring channels are neighbours in memory.
+// Column-transposing MXFP8 per group.  A workgroup owns 128 padded output
+// columns (four 32-blocks of tokens) x 128 channels.  Block b of the tile is
+// padded column range [p0 + 32b, +32) = tokens [m0_b, m0_b + n_b) of one
+// group (n_b < 32 at a group's end, 0 in padding).  The bf16 tile
+// [128 token slots][128 channels] (256-byte rows, 32 KB) arrives through
+// buffer-to-LDS DMA, slots past n_b as zeros.  Thread (pair p, block b) then
+// encodes channels 2p and 2p+1 of block b from 32 dword reads (one token row
+// per read, a wave covering one row: conflict-free) and writes each channel's
+// 32 codes as two 16-byte stores; the 4 blocks of a channel form one
+// contiguous 128-byte run of codes[channel][p0 .. p0+128).  Workgroups that
+// are neighbours in launch order take neighbouring channel tiles of the same
+// token rows.
 constexpr int COLT_TOK = 128;
-constexpr int COLT_CH = 256;
-constexpr int COLT_PITCH = COLT_CH + 8;  // bf16 elements; keeps 16-byte rows aligned
+constexpr int COLT_CH = 128;
+
+// Group of padded column pc: the last g with start(g) = 32 * (g + off[g]/32)
+// <= pc (starts strictly increase).  Wave-wide 64-ary search: one round of
+// loads for up to 64 groups.  Returns the group; lane l's (start, off) of
+// group base + l come back through `base`, `st`, `of0`, `of1` for the caller.
+__device__ __forceinline__ int colt_find_base(const int32_t* __restrict__ offsets, int ngroups, int64_t pc, int lane) {
+    int lo = 0, n = ngroups;
+    while (n > 64) {
+        const int step = (n + 63) / 64;
+        const int g = lo + lane * step;
+        const bool le = (g < lo + n) && (32 * ((int64_t)g + offsets[g] / 32) <= pc);
+        const int cnt = __builtin_popcountll(__ballot(le));
+        const int nlo = lo + max(cnt - 1, 0) * step;
+        n = min(step, lo + n - nlo);
+        lo = nlo;
+    }
+    const int g = lo + lane;
+    const bool le = (g < lo + n) && (32 * ((int64_t)g + offsets[g] / 32) <= pc);
+    return lo + max(__builtin_popcountll(__ballot(le)) - 1, 0);
+}
 
 __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
     const uint16_t* __restrict__ x, int64_t rows, int cols, int64_t ldx, const int32_t* __restrict__ offsets,
     int ngroups, int64_t P, uint8_t* __restrict__ codes, uint8_t* __restrict__ scale) {
-    __shared__ __align__(16) uint16_t tile[COLT_TOK * COLT_PITCH];
+    __shared__ __align__(16) uint8_t tile[COLT_TOK * COLT_CH * 2];
     __shared__ int64_t blk_m0[4];
     __shared__ int blk_n[4];
     const int t = threadIdx.x;
-    const int64_t p0 = (int64_t)blockIdx.x * COLT_TOK;
-    const int c_base = blockIdx.y * COLT_CH;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    // launch order: channel tile fastest, so concurrently running workgroups
+    // read neighbouring parts of the same token rows
+    const int nct = (cols + COLT_CH - 1) / COLT_CH;
+    const int64_t p0 = (int64_t)(blockIdx.x / nct) * COLT_TOK;
+    const int c_base = (int)(blockIdx.x % nct) * COLT_CH;
 
-    if (t < 4) {
-        // Group g starts at padded column 32*(g + offsets[g]/32), strictly
-        // increasing in g: find the last group starting at or before pc.
-        const int64_t pc = p0 + 32 * t;
-        int64_t m0 = 0;
-        int n = 0;
-        if (pc < P) {
-            int lo = 0, hi = ngroups - 1, g = -1;
-            while (lo <= hi) {
-                const int mid = (lo + hi) >> 1;
-                const int64_t st = 32 * ((int64_t)mid + offsets[mid] / 32);
-                if (st <= pc) { g = mid; lo = mid + 1; } else { hi = mid - 1; }
-            }
-            if (g >= 0) {
-                const int64_t st = 32 * ((int64_t)g + offsets[g] / 32);
-                const int64_t mb = offsets[g] + (pc - st);
-                const int64_t end = offsets[g + 1];
-                if (mb < end) {
-                    m0 = mb;
-                    n = (int)min((int64_t)32, end - mb);
-                }
-            }
-        }
-        blk_m0[t] = m0;
-        blk_n[t] = n;
-    }
-    __syncthreads();
-
-    // Stage: 128 token slots x 256 channels, 16 bytes per thread per step.
-    const int q = t & 31;
-    const int ch = c_base + 8 * q;
-#pragma unroll 4
-    for (int i = 0; i < COLT_TOK / 8; ++i) {
-        const int s = (t >> 5) + 8 * i;
-        const int b = s >> 5, ii = s & 31;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (ii < blk_n[b] && ch < cols)
-            val = ld_stream16(x + (blk_m0[b] + ii) * ldx + ch);
-        *reinterpret_cast<uint4*>(&tile[s * COLT_PITCH + 8 * q]) = val;
-    }
-    __syncthreads();
-
-    const int c = c_base + t;
-    if (c >= cols) return;
-    uint8_t* crow = codes + (int64_t)c * P;
-#pragma unroll 1
-    for (int b = 0; b < 4; ++b) {
-        const int64_t pc = p0 + 32 * b;
-        if (pc >= P) break;
-        uint32_t w[16];
+    if (wave == 0) {
+        // groups of the 4 blocks lie within g0 .. g0 + 3 (a group spans >= 32 columns)
+        const int g0 = __builtin_amdgcn_readfirstlane(colt_find_base(offsets, ngroups, p0, lane));
+        const int g = g0 + lane;
+        const bool have = g < ngroups;
+        const int32_t of0 = have ? offsets[g] : 0;
+        const int32_t of1 = have ? offsets[g + 1] : 0;
+        const int64_t st = 32 * ((int64_t)g + of0 / 32);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const uint32_t lo = tile[(32 * b + 2 * j) * COLT_PITCH + t];
-            const uint32_t hi = tile[(32 * b + 2 * j + 1) * COLT_PITCH + t];
-            w[j] = lo | (hi << 16);
+        for (int b = 0; b < 4; ++b) {
+            const int64_t pc = p0 + 32 * b;
+            const int k = max(__builtin_popcountll(__ballot(have && st <= pc)) - 1, 0);
+            const int64_t stk = 32 * ((int64_t)(g0 + k) + __builtin_amdgcn_readlane(of0, k) / 32);
+            const int64_t mb = __builtin_amdgcn_readlane(of0, k) + (pc - stk);
+            const int64_t end = __builtin_amdgcn_readlane(of1, k);
+            if (lane == 0) {
+                const bool ok = pc < P && mb < end;
+                blk_m0[b] = ok ? mb : 0;
+                blk_n[b] = ok ? (int)min((int64_t)32, end - mb) : 0;
+            }
         }
-        const MxBlock r = mx_encode(w);
-        uint4* o = reinterpret_cast<uint4*>(crow + pc);
-        o[0] = r.c0;
-        o[1] = r.c1;
-        scale[(pc >> 5) * cols + c] = (uint8_t)r.sbyte;  // block-major: coalesced across channels
     }
+    __syncthreads();
+
+    // DMA: instruction i of this wave covers tile rows 4 * (8 * wave + i) + lane / 16,
+    // 16 bytes (8 channels) per lane.  Offsets are taken from the first token
+    // of the tile, so they stay below 2^31 (host check: 258 * ldx < 2^31).
+    {
+        // first token of the tile: blocks run in token order, so the first
+        // block holding tokens has the smallest m0
+        int64_t mlo = 0;
+#pragma unroll
+        for (int b = 3; b >= 0; --b) mlo = blk_n[b] > 0 ? blk_m0[b] : mlo;
+        mlo = uniform_i64(mlo);
+        const i32x4 d = make_desc(uniform_ptr(x + mlo * ldx));
+        const uint32_t L = __builtin_amdgcn_readfirstlane(lds_addr(tile));
+        const int chunk = lane & 15;
+        const int ch = c_base + 8 * chunk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ins = 8 * wave + i;
+            const int row = 4 * ins + (lane >> 4);
+            const int b = row >> 5, ii = row & 31;
+            const bool ok = (ii < blk_n[b]) & (ch < cols);
+            const uint32_t off = (uint32_t)(((blk_m0[b] - mlo + ii) * ldx + ch) * 2);
+            dma16(d, ok ? off : OOB, L + 1024u * (uint32_t)ins);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+
+    const int pr = t & 63, b = t >> 6;  // channel pair, block (one block per wave)
+    const int64_t pc = p0 + 32 * b;
+    const int c = c_base + 2 * pr;
+    if (pc >= P || c >= cols) return;
+    uint32_t w0[16], w1[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t r0 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j) * 256 + 4 * pr]);
+        const uint32_t r1 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j + 1) * 256 + 4 * pr]);
+        w0[j] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // low halves: channel 2p, tokens 2j, 2j+1
+        w1[j] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // high halves: channel 2p+1
+    }
+    const MxBlock e0 = mx_encode(w0);
+    const MxBlock e1 = mx_encode(w1);
+    uint4* o0 = reinterpret_cast<uint4*>(codes + (int64_t)c * P + pc);
+    uint4* o1 = reinterpret_cast<uint4*>(codes + (int64_t)(c + 1) * P + pc);
+    o0[0] = e0.c0;
+    o0[1] = e0.c1;
+    o1[0] = e1.c0;
+    o1[1] = e1.c1;
+    uint8_t* sp = scale + (pc >> 5) * cols + c;  // block-major: coalesced across channels
+    sp[0] = (uint8_t)e0.sbyte;
+    sp[1] = (uint8_t)e1.sbyte;
 }
 
 // ------------------------------------------------------- debug encoders
@@ -315,7 +358,9 @@ hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows, int co
 hipError_t launch_quantize_mxfp8_colwise_t(const uint16_t* x, int64_t rows, int cols, int64_t ldx,
                                            const int32_t* offsets, int ngroups, int64_t P, uint8_t* codes,
                                            uint8_t* scale, hipStream_t s) {
-    const dim3 grid((unsigned)((P + COLT_TOK - 1) / COLT_TOK), (unsigned)((cols + COLT_CH - 1) / COLT_CH));
+    const int64_t nwg = (int64_t)((cols + COLT_CH - 1) / COLT_CH) * ((P + COLT_TOK - 1) / COLT_TOK);
+    if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // beyond the host-checked sizes
+    const dim3 grid((unsigned)nwg);
     hipLaunchKernelGGL(k_quantize_mxfp8_colwise_t, grid, dim3(256), 0, s, x, rows, cols, ldx, offsets, ngroups, P,
                        codes, scale);
     return hipGetLastError();
