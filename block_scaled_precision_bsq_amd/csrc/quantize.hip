@@ -163,29 +163,64 @@ __device__ __forceinline__ MxBlock mx_encode(const uint32_t (&w)[16]) {
     return r;
 }
 
-// Row-wise MXFP8: one thread per 32-element block; neighbouring threads take
-// neighbouring blocks of a row (64-byte loads, 32-byte stores, contiguous).
+// Row-wise MXFP8.  A workgroup owns 128 rows x 32 blocks (1024 columns);
+// neighbouring threads take neighbouring blocks of a row (64-byte loads and
+// 32-byte code stores, contiguous across a wave).  Scales are block-major, so
+// a thread's scale byte is `rows` bytes away from its neighbour's: the bytes
+// are gathered in LDS as [block][row] and leave as one 128-byte run per block
+// (16-byte stores when every run is 16-byte aligned, bytes otherwise).
+constexpr int MXR_ROWS = 128;
+constexpr int MXR_BLK = 32;
+constexpr int MXR_PITCH = MXR_ROWS + 8;  // bytes per block row in LDS (bank spread)
+
+template <bool ALIGNED16>
 __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* __restrict__ x, int64_t rows,
                                                                 int cols, int64_t ldx,
                                                                 uint8_t* __restrict__ codes,
                                                                 uint8_t* __restrict__ scale) {
+    __shared__ __align__(16) uint8_t sb[MXR_BLK * MXR_PITCH];
     const int nb = cols >> 5;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= rows * nb) return;
-    const int64_t row = gid / nb;
-    const int b = (int)(gid - row * nb);
-    const uint4* p = reinterpret_cast<const uint4*>(x + row * ldx + 32 * b);
-    uint32_t w[16];
+    const int nbt = (nb + MXR_BLK - 1) / MXR_BLK;
+    const int64_t r0 = (int64_t)(blockIdx.x / nbt) * MXR_ROWS;
+    const int b0 = (int)(blockIdx.x % nbt) * MXR_BLK;
+    const int t = threadIdx.x;
+    const int bl = t & 31;       // block within the tile
+    const int b = b0 + bl;
+#pragma unroll 4
+    for (int it = 0; it < MXR_ROWS / 8; ++it) {
+        const int rl = 8 * it + (t >> 5);
+        const int64_t row = r0 + rl;
+        if (row < rows && b < nb) {
+            const uint4* p = reinterpret_cast<const uint4*>(x + row * ldx + 32 * b);
+            uint32_t w[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint4 t = ld_stream16(p + q);
-        w[4 * q] = t.x; w[4 * q + 1] = t.y; w[4 * q + 2] = t.z; w[4 * q + 3] = t.w;
+            for (int q = 0; q < 4; ++q) {
+                const uint4 v = ld_stream16(p + q);
+                w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+            }
+            const MxBlock r = mx_encode(w);
+            uint4* o = reinterpret_cast<uint4*>(codes + row * (int64_t)cols + 32 * b);
+            o[0] = r.c0;
+            o[1] = r.c1;
+            sb[bl * MXR_PITCH + rl] = (uint8_t)r.sbyte;
+        }
     }
-    const MxBlock r = mx_encode(w);
-    uint4* o = reinterpret_cast<uint4*>(codes + row * (int64_t)cols + 32 * b);
-    o[0] = r.c0;
-    o[1] = r.c1;
-    scale[(int64_t)b * rows + row] = (uint8_t)r.sbyte;  // block-major scales
+    __syncthreads();
+    // block bl2 = t / 8 leaves as bytes [16 * (t % 8), +16) of its 128-row run
+    const int bl2 = t >> 3, q = t & 7;
+    const int bb = b0 + bl2;
+    const int64_t rr = r0 + 16 * q;
+    if (bb >= nb || rr >= rows) return;
+    uint8_t* dst = scale + (int64_t)bb * rows + rr;
+    const uint8_t* src = &sb[bl2 * MXR_PITCH + 16 * q];
+    if (ALIGNED16 && rr + 16 <= rows) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(src);
+        const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+        const int n = (int)min((int64_t)16, rows - rr);
+        for (int k = 0; k < n; ++k) dst[k] = src[k];
+    }
 }
 
 // Column-transposing MXFP8 per group.  A workgroup owns 128 padded output
@@ -349,9 +384,16 @@ hipError_t launch_quantize_nvfp4v(const uint16_t* x, int64_t rows, int cols, int
 
 hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
                                          uint8_t* scale, hipStream_t s) {
-    const int64_t nblk = rows * (cols / 32);
-    hipLaunchKernelGGL(k_quantize_mxfp8_rowwise, dim3((unsigned)((nblk + 255) / 256)), dim3(256), 0, s, x, rows,
-                       cols, ldx, codes, scale);
+    const int nbt = (cols / 32 + MXR_BLK - 1) / MXR_BLK;
+    const int64_t nwg = ((rows + MXR_ROWS - 1) / MXR_ROWS) * nbt;
+    if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const bool a16 = (rows % 16 == 0) && ((reinterpret_cast<uintptr_t>(scale) & 15) == 0);
+    if (a16)
+        hipLaunchKernelGGL(k_quantize_mxfp8_rowwise<true>, dim3((unsigned)nwg), dim3(256), 0, s, x, rows, cols, ldx,
+                           codes, scale);
+    else
+        hipLaunchKernelGGL(k_quantize_mxfp8_rowwise<false>, dim3((unsigned)nwg), dim3(256), 0, s, x, rows, cols, ldx,
+                           codes, scale);
     return hipGetLastError();
 }
 

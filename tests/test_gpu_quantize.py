@@ -162,10 +162,13 @@ def test_nvfp4v_strided_input(orc, bsq_gpu):
 
 # ------------------------------------------------------------------ MXFP8
 
-@pytest.mark.parametrize("cols", [32, 96, 2048, 7168])
-def test_mxfp8_rowwise_parity(orc, bsq_gpu, cols):
-    rng = rng_for(2, salt=100 + cols)
-    x = make_quantize_input(rng, 129, cols)
+@pytest.mark.parametrize("rows,cols", [(129, 32), (129, 96), (129, 2048), (129, 7168), (384, 1056), (16, 7168)])
+def test_mxfp8_rowwise_parity(orc, bsq_gpu, rows, cols):
+    """Row tiles of 128 rows and 1024 columns: partial row tiles, partial
+    column tiles, and both scale write paths (16-byte runs when the row count
+    is a multiple of 16, bytes otherwise)."""
+    rng = rng_for(2, salt=100 + cols + rows)
+    x = make_quantize_input(rng, rows, cols)
     x[0] = 0
     x[1, :32] = bf16(np.full(32, 2.0 ** -130))
     x[2] = bf16(rng.standard_normal(cols) * 2.0 ** 125)
