@@ -132,6 +132,8 @@ bsq_status bsq_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_bscale,
         return BSQ_ERR_UNSUPPORTED;
     // per-tile buffer offsets are 32-bit: 256 rows of codes/scales
     if (256 * (k / 2) >= kMaxBufferOffset || m_total >= (int64_t)1 << 31) return BSQ_ERR_UNSUPPORTED;
+    // per-tile output offsets are 32-bit: 256 rows of n outputs
+    if (256 * n * (y_dtype == BSQ_F32 ? 4 : 2) >= kMaxBufferOffset) return BSQ_ERR_UNSUPPORTED;
     if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, n, k))
         return BSQ_ERR_WORKSPACE_TOO_SMALL;
     return from_hip(bsq::launch_gemm_fwd_nvfp4v(a_codes, a_bscale, a_rscale, w_codes, w_bscale, w_rscale, offsets,

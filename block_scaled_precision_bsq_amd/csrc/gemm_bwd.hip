@@ -52,11 +52,6 @@ struct BwdSmem {
     uint32_t sb[2][4 * PIPE_ROWS];
 };
 
-// 128-byte rows hold 8 chunks of 16 bytes; chunk c of row r lives in slot
-// c ^ swz8(r).  A 16-lane quarter of a fragment read covers 16 consecutive
-// rows at one chunk: rows of equal parity share 8-chunk halves of the 64 LDS
-// banks and swz8 = (r >> 1) & 7 spreads them over all 8 slots.
-__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 // One output tile of C[i][j] = sum_r A[i][r] B[j][r].
 struct TileOps {

@@ -1,4 +1,4 @@
-// LDS staging pipeline shared by the grouped GEMM kernels (gfx950).
+// LDS staging helpers shared by the grouped GEMM and quantize kernels (gfx950).
 //
 // Operand tiles travel global -> LDS through the buffer-load-to-LDS path
 // ("buffer_load_dwordx4 ... lds"): each wave instruction writes 64 lanes x 16
@@ -30,6 +30,12 @@ constexpr int PIPE_STAGE_BYTES = PIPE_ROWS * PIPE_BK;
 constexpr int PIPE_NST = 4;                     // ring depth
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// 128-byte rows hold 8 chunks of 16 bytes; chunk c of row r lives in slot
+// c ^ swz8(r).  A 16-lane quarter of a fragment read covers 16 consecutive
+// rows at one chunk: rows of equal parity share 8-chunk halves of the 64 LDS
+// banks and swz8 = (r >> 1) & 7 spreads them over all 8 slots.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 // Byte offset of logical 16-byte chunk c of row r inside a stage buffer.
 __device__ __forceinline__ int swz_off(int r, int c) { return r * PIPE_BK + 16 * (c ^ swz(r)); }
