@@ -71,18 +71,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     extern __shared__ __align__(16) uint8_t smem_raw[];
     __shared__ int s_tile;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    const int tid0 = threadIdx.x;
     // wave-uniform by construction; readfirstlane lets the compiler keep
     // everything derived from it in SGPRs
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int lr = lane & 31, g = lane >> 5;
     const int xcd = blockIdx.x & 7;
     constexpr int esz = OUT_F32 ? 4 : 2;
     const int total = p.plan[PLAN_TOTAL];
-    const int32_t* start = plan_start(p.plan);
-    const int32_t* order = plan_order(p.plan, p.E);
     int dq = 0;
 
     // 32-bit LDS byte addresses of the ring (DMA targets go through M0)
@@ -93,36 +89,49 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     const __attribute__((address_space(3))) uint8_t* lds =
         (const __attribute__((address_space(3))) uint8_t*)(smem_raw);
 
-    // DMA lane geometry: code instruction i (0..7) of this wave covers rows
-    // 64 * wave + 8 * i + lane / 8; the lane fetches logical chunk
-    // (lane & 7) ^ swz8(row) into slot lane & 7.  swz8(row) depends on lane / 8
-    // and on the parity of i.
-    const int drow0 = 64 * wave + (lane >> 3);
-    const uint32_t dch0 = (uint32_t)((lane & 7) ^ swz8(lane >> 3));        // even i
-    const uint32_t dch1 = (uint32_t)((lane & 7) ^ swz8(8 + (lane >> 3)));  // odd i
-    // Fragment read geometry: lane (lr, g) of k step h reads chunks 4h + g and
-    // 4h + g + 2 of row lr of each 32-row group; swz8(row) = swz8(lr), and
-    // (4h + g + 2d) ^ swz8 = (g ^ swz8) ^ (4h + 2d).
-    const uint32_t fr = (uint32_t)(lr * SS_BK + 16 * (g ^ swz8(lr)));
-    const uint32_t fa = offsetof(BwdSmem, a) + (uint32_t)(wm * 128 * SS_BK);
-    const uint32_t fb = offsetof(BwdSmem, b) + (uint32_t)(wn * 128 * SS_BK);
-    const uint32_t fsa = offsetof(BwdSmem, sa) + 4u * (uint32_t)(256 * g + wm * 128 + lr);
-    const uint32_t fsb = offsetof(BwdSmem, sb) + 4u * (uint32_t)(256 * g + wn * 128 + lr);
+    // decode tables in LDS behind the staging buffers (when they fit)
+    __attribute__((address_space(3))) int32_t* tab =
+        (__attribute__((address_space(3))) int32_t*)(smem_raw + sizeof(BwdSmem));
+    const bool tab_lds = p.E <= LDS_TABLE_MAX_E;
+    if (tab_lds) fill_lds_tables(tab, p.plan, p.offsets, p.E);
+    if (tid0 == 0) s_tile = claim_tile(p.plan, xcd, total, dq);
+    __syncthreads();
+    int tile = __builtin_amdgcn_readfirstlane(s_tile);  // uniform: keeps tile state in SGPRs
 
     for (;;) {
-        if (tid == 0) s_tile = claim_tile(p.plan, xcd, total, dq);
-        __syncthreads();
-        const int tile = __builtin_amdgcn_readfirstlane(s_tile);  // uniform: keeps tile state in SGPRs
-        __syncthreads();
         if (tile < 0) break;
+        // Lane constants are rebuilt per tile from an opaque copy of the
+        // thread index: hoisted out of the tile loop they would stay live
+        // through every phase and push the kernel into spills.
+        int tid = tid0;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int lr = lane & 31, g = lane >> 5;
+        // DMA lane geometry: code instruction i (0..7) of this wave covers rows
+        // 64 * wave + 8 * i + lane / 8; the lane fetches logical chunk
+        // (lane & 7) ^ swz8(row) into slot lane & 7.  swz8(row) depends on lane / 8
+        // and on the parity of i.
+        const int drow0 = 64 * wave + (lane >> 3);
+        const uint32_t dch0 = (uint32_t)((lane & 7) ^ swz8(lane >> 3));        // even i
+        const uint32_t dch1 = (uint32_t)((lane & 7) ^ swz8(8 + (lane >> 3)));  // odd i
+        // Fragment read geometry: lane (lr, g) of k step h reads chunks 4h + g and
+        // 4h + g + 2 of row lr of each 32-row group; swz8(row) = swz8(lr), and
+        // (4h + g + 2d) ^ swz8 = (g ^ swz8) ^ (4h + 2d).
+        const uint32_t fr = (uint32_t)(lr * SS_BK + 16 * (g ^ swz8(lr)));
+        const uint32_t fa = offsetof(BwdSmem, a) + (uint32_t)(wm * 128 * SS_BK);
+        const uint32_t fb = offsetof(BwdSmem, b) + (uint32_t)(wn * 128 * SS_BK);
+        const uint32_t fsa = offsetof(BwdSmem, sa) + 4u * (uint32_t)(256 * g + wm * 128 + lr);
+        const uint32_t fsb = offsetof(BwdSmem, sb) + 4u * (uint32_t)(256 * g + wn * 128 + lr);
 
-        // Tile decode; readfirstlane marks the results wave-uniform so that
-        // addresses and buffer descriptors stay in SGPRs.
-        const int pos = find_position(start, p.E, tile);
-        const int e = __builtin_amdgcn_readfirstlane(order[pos]);
-        const int local = __builtin_amdgcn_readfirstlane(tile - start[pos]);
-        const int64_t off0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
-        const int64_t off1 = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+        // claim the next tile now; the atomic's latency hides behind this one
+        int next_tile = 0;
+        if (tid == 0) next_tile = claim_tile(p.plan, xcd, total, dq);
+
+        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tile);
+        const int e = tr.e;
+        const int local = tr.local;
+        const int64_t off0 = tr.off0;
+        const int64_t off1 = tr.off1;
         TileOps op;
         if (!p.wgrad) {
             // dX[m][k] = sum_n dY[m][n] Wt_e[k][n]
@@ -187,32 +196,36 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         // wave), in 12 parts of 2 so they can sit between MFMAs: parts 0..7
         // move code rows (A and B of instruction i), parts 8..11 scale blocks.
         // A 16-byte chunk or a 32-element scale block past R reads as zero.
-        auto issue_part = [&](int S, int part) {
+        auto issue_part = [&](int S, auto PC) {
+            constexpr int part = decltype(PC)::value;
             const uint32_t q = (uint32_t)S & 1;
             const uint32_t kbase = (uint32_t)S * SS_BK;
-            if (part < 8) {
-                const int i = part;
+            if constexpr (part < 8) {
+                constexpr int i = part;
                 const int row = drow0 + 8 * i;
                 const uint32_t ch = (i & 1) ? dch1 : dch0;
                 const bool okk = kbase + 16 * ch < R;
                 const uint32_t ko = kbase + 16 * ch;
-                const uint32_t ldst = q * SS_TILE + 1024u * (uint32_t)(8 * wave + i);
-                dma16(dA, (okk & (row < op.rows_a)) ? vra + (uint32_t)(8 * i) * lda + ko : OOB, LA + ldst);
-                dma16(dB, (okk & (row < op.rows_b)) ? vrb + (uint32_t)(8 * i) * ldb + ko : OOB, LB + ldst);
+                const uint32_t slot = q * SS_TILE + 8192u * (uint32_t)wave;
+                dma16(dA, (okk & (row < op.rows_a)) ? vra + (uint32_t)(8 * i) * lda + ko : OOB,
+                      lds_at<1024u * i>(LA + slot));
+                dma16(dB, (okk & (row < op.rows_b)) ? vrb + (uint32_t)(8 * i) * ldb + ko : OOB,
+                      lds_at<1024u * i>(LB + slot));
             } else {
-                const int i = part - 8;
+                constexpr int i = part - 8;
                 const int ins = 4 * wave + i;
                 const uint32_t blk = 4 * (uint32_t)S + (uint32_t)(ins >> 2);
                 const bool oks = blk * 32 < R;
                 const uint32_t sblk = 4 * (uint32_t)S;
-                const uint32_t ldst = 4u * (q * 1024u + 64u * (uint32_t)ins);
-                dma1(dAs, oks ? vsa[i] + sblk * ldas : OOB, LSA + ldst);
-                dma1(dBs, oks ? vsb[i] + sblk * ldbs : OOB, LSB + ldst);
+                const uint32_t slot = 4u * (q * 1024u + 256u * (uint32_t)wave);
+                dma1(dAs, oks ? vsa[i] + sblk * ldas : OOB, lds_at<256u * i>(LSA + slot));
+                dma1(dBs, oks ? vsb[i] + sblk * ldbs : OOB, lds_at<256u * i>(LSB + slot));
             }
         };
         auto issue = [&](int S) {
-#pragma unroll
-            for (int part = 0; part < 12; ++part) issue_part(S, part);
+            issue_part(S, IC<0>{}); issue_part(S, IC<1>{}); issue_part(S, IC<2>{}); issue_part(S, IC<3>{});
+            issue_part(S, IC<4>{}); issue_part(S, IC<5>{}); issue_part(S, IC<6>{}); issue_part(S, IC<7>{});
+            issue_part(S, IC<8>{}); issue_part(S, IC<9>{}); issue_part(S, IC<10>{}); issue_part(S, IC<11>{});
         };
         // Fragments of k step t (ring slot (t / 2) % 2, half h = t % 2): lane
         // (row, g) takes logical chunks 4h + g and 4h + g + 2 of its row (the
@@ -277,7 +290,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                 const int i = k >> 2, j = k & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
                                                                           cur.sa[i], 0, cur.sb[j]);
-                if (k < 12) issue_part(S, k);
+                switch (k) {
+                    case 0: issue_part(S, IC<0>{}); break;
+                    case 1: issue_part(S, IC<1>{}); break;
+                    case 2: issue_part(S, IC<2>{}); break;
+                    case 3: issue_part(S, IC<3>{}); break;
+                    case 4: issue_part(S, IC<4>{}); break;
+                    case 5: issue_part(S, IC<5>{}); break;
+                    case 6: issue_part(S, IC<6>{}); break;
+                    case 7: issue_part(S, IC<7>{}); break;
+                    case 8: issue_part(S, IC<8>{}); break;
+                    case 9: issue_part(S, IC<9>{}); break;
+                    case 10: issue_part(S, IC<10>{}); break;
+                    case 11: issue_part(S, IC<11>{}); break;
+                    default: break;
+                }
                 if (k >= 4 && k < 12) read_part(t + 1, nxt, k - 4);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -360,11 +387,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                     }
                 }
                 // every wave's reads of this pass are done before the next
-                // pass (or the next tile's DMA) overwrites the staging area
+                // pass (or the next tile's DMA) overwrites the staging area;
+                // the last barrier also publishes the next tile
+                if (pass == 1 && tid == 0) s_tile = next_tile;
                 wait_lgkmcnt0();
                 block_barrier();
             }
         }
+        tile = __builtin_amdgcn_readfirstlane(s_tile);
     }
 }
 
@@ -383,17 +413,20 @@ hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s) {
     static bool attr_set = false;  // idempotent; racing writers set the same value
     if (!attr_set) {
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(BwdSmem));
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(sizeof(BwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
         if (err != hipSuccess) return err;
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(BwdSmem));
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(sizeof(BwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
         if (err != hipSuccess) return err;
         attr_set = true;
     }
+    const size_t lds = sizeof(BwdSmem) + lds_table_bytes(args.E);
     if (args.out_f32)
-        hipLaunchKernelGGL(k_gemm_bwd_mxfp8<true>, dim3(grid), dim3(256), sizeof(BwdSmem), s, args);
+        hipLaunchKernelGGL(k_gemm_bwd_mxfp8<true>, dim3(grid), dim3(256), lds, s, args);
     else
-        hipLaunchKernelGGL(k_gemm_bwd_mxfp8<false>, dim3(grid), dim3(256), sizeof(BwdSmem), s, args);
+        hipLaunchKernelGGL(k_gemm_bwd_mxfp8<false>, dim3(grid), dim3(256), lds, s, args);
     return hipGetLastError();
 }
 

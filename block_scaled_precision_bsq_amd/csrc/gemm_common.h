@@ -81,6 +81,58 @@ __device__ __forceinline__ int find_position(const int32_t* start, int E, int t)
     return lo;
 }
 
+// Tile decode.  A tile index maps to (expert, tile within the expert) through
+// the planner's per-expert tile prefix and expert order, and the expert's
+// token range comes from `offsets`.  When the expert count is small enough,
+// the GEMM kernels copy the three arrays into LDS behind their staging
+// buffers at kernel start, so a decode costs a few LDS reads instead of a
+// chain of dependent global loads; otherwise they read the global arrays.
+constexpr int LDS_TABLE_MAX_E = 800;
+__host__ __device__ inline size_t lds_table_bytes(int E) {
+    return E <= LDS_TABLE_MAX_E ? (size_t)4 * (3 * (size_t)E + 2) : 0;
+}
+
+struct TileRef {
+    int e, local;
+    int64_t off0, off1;
+};
+
+template <class P>
+__device__ __forceinline__ TileRef decode_tile(P start, P order, P offs, int E, int t) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (start[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    TileRef r;
+    r.e = __builtin_amdgcn_readfirstlane(order[lo]);
+    r.local = __builtin_amdgcn_readfirstlane(t - start[lo]);
+    r.off0 = __builtin_amdgcn_readfirstlane(offs[r.e]);
+    r.off1 = __builtin_amdgcn_readfirstlane(offs[r.e + 1]);
+    return r;
+}
+
+typedef const __attribute__((address_space(3))) int32_t* lds_i32p;
+
+// LDS copy of the decode arrays (start[E+1], order[E], offsets[E+1]) at `tab`;
+// every thread of the workgroup takes part; the caller synchronizes.
+__device__ __forceinline__ void fill_lds_tables(__attribute__((address_space(3))) int32_t* tab, const int32_t* plan,
+                                                const int32_t* offsets, int E) {
+    const int32_t* start = plan_start(plan);
+    const int32_t* order = plan_order(plan, E);
+    for (int i = threadIdx.x; i <= E; i += blockDim.x) {
+        tab[i] = start[i];
+        tab[2 * E + 1 + i] = offsets[i];
+        if (i < E) tab[E + 1 + i] = order[i];
+    }
+}
+
+__device__ __forceinline__ TileRef decode_tile_any(bool in_lds, const __attribute__((address_space(3))) int32_t* tab,
+                                                   const int32_t* plan, const int32_t* offsets, int E, int t) {
+    if (in_lds) return decode_tile<lds_i32p>(tab, tab + E + 1, tab + 2 * E + 1, E, t);
+    return decode_tile<const int32_t*>(plan_start(plan), plan_order(plan, E), offsets, E, t);
+}
+
 // Arguments of the MXFP8 backward GEMM kernel (one launch computes either the
 // dgrad or the wgrad tiles).
 struct BwdArgs {

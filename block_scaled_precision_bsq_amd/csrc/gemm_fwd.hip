@@ -110,8 +110,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     const int nsup = (int)((p.K + FS_K - 1) / FS_K);
     const int NT = (int)((p.N + FWD_BN - 1) / FWD_BN);
     const int total = p.plan[PLAN_TOTAL];
-    const int32_t* start = plan_start(p.plan);
-    const int32_t* order = plan_order(p.plan, p.E);
     int dq = 0;
 
     // 32-bit LDS byte addresses (DMA targets go through M0)
@@ -139,18 +137,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     const uint32_t fsa = offsetof(FwdSmem, sa) + (uint32_t)((wm * 128 + lr) * FS_SB);
     const uint32_t fsb = offsetof(FwdSmem, sb) + (uint32_t)((wn * 128 + lr) * FS_SB);
 
-    for (;;) {
-        if (tid == 0) s_tile = claim_tile(p.plan, xcd, total, dq);
-        __syncthreads();
-        const int tile = __builtin_amdgcn_readfirstlane(s_tile);  // uniform: keeps tile state in SGPRs
-        __syncthreads();
-        if (tile < 0) break;
+    // decode tables in LDS behind the staging buffers (when they fit)
+    __attribute__((address_space(3))) int32_t* tab =
+        (__attribute__((address_space(3))) int32_t*)(smem_raw + sizeof(FwdSmem));
+    const bool tab_lds = p.E <= LDS_TABLE_MAX_E;
+    if (tab_lds) fill_lds_tables(tab, p.plan, p.offsets, p.E);
+    if (tid == 0) s_tile = claim_tile(p.plan, xcd, total, dq);
+    __syncthreads();
+    int tile = __builtin_amdgcn_readfirstlane(s_tile);  // uniform: keeps tile state in SGPRs
 
-        const int pos = find_position(start, p.E, tile);
-        const int e = __builtin_amdgcn_readfirstlane(order[pos]);
-        const int local = __builtin_amdgcn_readfirstlane(tile - start[pos]);
-        const int64_t off0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
-        const int64_t off1 = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+    for (;;) {
+        if (tile < 0) break;
+        // claim the next tile now; the atomic's latency hides behind this one
+        int next_tile = 0;
+        if (tid == 0) next_tile = claim_tile(p.plan, xcd, total, dq);
+
+        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tile);
+        const int e = tr.e;
+        const int local = tr.local;
+        const int64_t off0 = tr.off0;
+        const int64_t off1 = tr.off1;
         int mt, nt;
         grouped_tile(local, (int)((off1 - off0 + FWD_BM - 1) / FWD_BM), NT, mt, nt);
         const int64_t m_base = uniform_i64(off0 + (int64_t)mt * FWD_BM);
@@ -358,11 +364,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
                     }
                 }
                 // every wave's reads of this pass are done before the next
-                // pass (or the next tile's DMA) overwrites the staging area
+                // pass (or the next tile's DMA) overwrites the staging area;
+                // the last barrier also publishes the next tile
+                if (pass == 1 && tid == 0) s_tile = next_tile;
                 wait_lgkmcnt0();
                 block_barrier();
             }
         }
+        tile = __builtin_amdgcn_readfirstlane(s_tile);
     }
 }
 
@@ -378,18 +387,21 @@ hipError_t launch_gemm_fwd_nvfp4v(const uint8_t* a_codes, const uint8_t* a_bscal
     static bool attr_set = false;  // idempotent; racing writers set the same value
     if (!attr_set) {
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FwdSmem));
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(sizeof(FwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
         if (err != hipSuccess) return err;
         err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FwdSmem));
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(sizeof(FwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
         if (err != hipSuccess) return err;
         attr_set = true;
     }
     FwdArgs p{a_codes, a_bscale, a_rscale, w_codes, w_bscale, w_rscale, offsets, E, N, K, y, y_f32, plan};
+    const size_t lds = sizeof(FwdSmem) + lds_table_bytes(E);
     if (y_f32)
-        hipLaunchKernelGGL(k_gemm_fwd_nvfp4v<true>, dim3(grid), dim3(256), sizeof(FwdSmem), s, p);
+        hipLaunchKernelGGL(k_gemm_fwd_nvfp4v<true>, dim3(grid), dim3(256), lds, s, p);
     else
-        hipLaunchKernelGGL(k_gemm_fwd_nvfp4v<false>, dim3(grid), dim3(256), sizeof(FwdSmem), s, p);
+        hipLaunchKernelGGL(k_gemm_fwd_nvfp4v<false>, dim3(grid), dim3(256), lds, s, p);
     return hipGetLastError();
 }
 

@@ -20,9 +20,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace bsq {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// compile-time index for generic lambdas (schedule slots, ring parts)
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 constexpr int PIPE_ROWS = 256;                  // rows per operand tile
 constexpr int PIPE_BK = 64;                     // bytes per row per stage
@@ -75,6 +81,15 @@ __device__ __forceinline__ void dma1(i32x4 desc, uint32_t voff, uint32_t lds_bas
     lds_base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_ubyte %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
+}
+
+// LDS target base + OFF with the base laundered through an empty asm: the
+// compiler then adds OFF right at the DMA instead of hoisting one live SGPR
+// per (instruction, ring slot) out of the loops.
+template <uint32_t OFF>
+__device__ __forceinline__ uint32_t lds_at(uint32_t base) {
+    asm volatile("" : "+s"(base));
+    return base + OFF;
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
