@@ -45,13 +45,20 @@ constexpr int SS_BK = 128;                       // bytes of k per row per super
 constexpr int SS_TILE = PIPE_ROWS * SS_BK;       // one operand's super-stage (32 KB)
 constexpr int SS_DMA = 24;                       // DMA instructions per wave per super-stage
 
-struct BwdSmem {
-    uint8_t a[2][SS_TILE];
-    uint8_t b[2][SS_TILE];
-    uint32_t sa[2][4 * PIPE_ROWS];  // E8M0 byte of (k block, row) in dword block*256 + row
-    uint32_t sb[2][4 * PIPE_ROWS];
+// One ring slot: codes of both operands and their scale bytes (one dword per
+// (k block, row): block * 256 + row).  Slot-major so that a whole slot is
+// one contiguous region -- the epilogue stages its output through slot 1
+// while the next tile's first super-stage lands in slot 0.
+struct BwdSlot {
+    uint8_t a[SS_TILE];
+    uint8_t b[SS_TILE];
+    uint32_t sa[4 * PIPE_ROWS];
+    uint32_t sb[4 * PIPE_ROWS];
 };
-
+struct BwdSmem {
+    BwdSlot slot[2];
+};
+constexpr uint32_t SLOT_BYTES = sizeof(BwdSlot);
 
 // One output tile of C[i][j] = sum_r A[i][r] B[j][r].
 struct TileOps {
@@ -64,6 +71,18 @@ struct TileOps {
 struct BwdFrag {
     int8v a[4], b[4];
     int sa[4], sb[4];
+};
+
+// Per-tile DMA state: buffer descriptors, leading dimensions and the lane
+// offsets at k = 0 (rows past the tile read as zero).
+struct BwdTile {
+    i32x4 dA, dB, dAs, dBs;
+    uint32_t lda, ldb, ldas, ldbs, R;
+    int rows_a, rows_b, nsteps;
+    char* c;
+    uint32_t ldcb;
+    uint32_t vra, vrb;
+    uint32_t vsa[4], vsb[4];
 };
 
 template <bool OUT_F32>
@@ -81,15 +100,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     const int total = p.plan[PLAN_TOTAL];
     int dq = 0;
 
-    // 32-bit LDS byte addresses of the ring (DMA targets go through M0)
+    // 32-bit LDS byte address of the ring (DMA targets go through M0)
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
-    const uint32_t LA = lds0 + offsetof(BwdSmem, a), LB = lds0 + offsetof(BwdSmem, b);
-    const uint32_t LSA = lds0 + offsetof(BwdSmem, sa), LSB = lds0 + offsetof(BwdSmem, sb);
-    // fragment reads address the same buffers relative to smem_raw
     const __attribute__((address_space(3))) uint8_t* lds =
         (const __attribute__((address_space(3))) uint8_t*)(smem_raw);
 
-    // decode tables in LDS behind the staging buffers (when they fit)
+    // decode tables in LDS behind the ring (when they fit)
     __attribute__((address_space(3))) int32_t* tab =
         (__attribute__((address_space(3))) int32_t*)(smem_raw + sizeof(BwdSmem));
     const bool tab_lds = p.E <= LDS_TABLE_MAX_E;
@@ -97,136 +113,150 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     if (tid0 == 0) s_tile = claim_tile(p.plan, xcd, total, dq);
     __syncthreads();
     int tile = __builtin_amdgcn_readfirstlane(s_tile);  // uniform: keeps tile state in SGPRs
+    if (tile < 0) return;
 
-    for (;;) {
-        if (tile < 0) break;
-        // Lane constants are rebuilt per tile from an opaque copy of the
-        // thread index: hoisted out of the tile loop they would stay live
-        // through every phase and push the kernel into spills.
-        int tid = tid0;
-        asm volatile("" : "+v"(tid));
-        const int lane = tid & 63;
-        const int lr = lane & 31, g = lane >> 5;
-        // DMA lane geometry: code instruction i (0..7) of this wave covers rows
-        // 64 * wave + 8 * i + lane / 8; the lane fetches logical chunk
-        // (lane & 7) ^ swz8(row) into slot lane & 7.  swz8(row) depends on lane / 8
-        // and on the parity of i.
-        const int drow0 = 64 * wave + (lane >> 3);
-        const uint32_t dch0 = (uint32_t)((lane & 7) ^ swz8(lane >> 3));        // even i
-        const uint32_t dch1 = (uint32_t)((lane & 7) ^ swz8(8 + (lane >> 3)));  // odd i
-        // Fragment read geometry: lane (lr, g) of k step h reads chunks 4h + g and
-        // 4h + g + 2 of row lr of each 32-row group; swz8(row) = swz8(lr), and
-        // (4h + g + 2d) ^ swz8 = (g ^ swz8) ^ (4h + 2d).
-        const uint32_t fr = (uint32_t)(lr * SS_BK + 16 * (g ^ swz8(lr)));
-        const uint32_t fa = offsetof(BwdSmem, a) + (uint32_t)(wm * 128 * SS_BK);
-        const uint32_t fb = offsetof(BwdSmem, b) + (uint32_t)(wn * 128 * SS_BK);
-        const uint32_t fsa = offsetof(BwdSmem, sa) + 4u * (uint32_t)(256 * g + wm * 128 + lr);
-        const uint32_t fsb = offsetof(BwdSmem, sb) + 4u * (uint32_t)(256 * g + wn * 128 + lr);
+    // Lane constants come from an opaque copy of the thread index, rebuilt
+    // per tile: hoisted out of the tile loop they would stay live through
+    // every phase and push the kernel into spills.
+    auto lane_of = [&]() {
+        int t = tid0;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
 
-        // claim the next tile now; the atomic's latency hides behind this one
-        int next_tile = 0;
-        if (tid == 0) next_tile = claim_tile(p.plan, xcd, total, dq);
-
-        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tile);
+    auto setup = [&](int tl) -> BwdTile {
+        const int lane = lane_of() & 63;
+        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tl);
         const int e = tr.e;
-        const int local = tr.local;
-        const int64_t off0 = tr.off0;
-        const int64_t off1 = tr.off1;
-        TileOps op;
+        const int64_t off0 = tr.off0, off1 = tr.off1;
+        const uint8_t *a, *as, *b, *bs;
+        int64_t lda, ldas, ldb, ldbs, R, ldc;
+        int rows_a, rows_b;
+        char* c;
         if (!p.wgrad) {
             // dX[m][k] = sum_n dY[m][n] Wt_e[k][n]
             const int KT = (int)((p.K + BWD_BN - 1) / BWD_BN);
             int mt, kt;
-            grouped_tile(local, (int)((off1 - off0 + BWD_BM - 1) / BWD_BM), KT, mt, kt);
+            grouped_tile(tr.local, (int)((off1 - off0 + BWD_BM - 1) / BWD_BM), KT, mt, kt);
             const int64_t m0 = off0 + (int64_t)mt * BWD_BM, k0 = (int64_t)kt * BWD_BN;
             const int64_t cw = (int64_t)e * (p.N + 32);  // 32*(e + e*N/32): segment start of W_e
             // block-major scales: block j of rows r0.. starts at base + j * rows_total + r0
-            op.a = p.dy_codes + m0 * p.N; op.as = p.dy_scale + m0;
-            op.lda = p.N; op.ldas = p.m_total; op.rows_a = (int)min((int64_t)BWD_BM, off1 - m0);
-            op.b = p.wt_codes + k0 * p.Pw + cw; op.bs = p.wt_scale + (cw / 32) * p.K + k0;
-            op.ldb = p.Pw; op.ldbs = p.K; op.rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
-            op.R = p.N;
-            op.c = reinterpret_cast<char*>(p.out) + (m0 * p.K + k0) * esz; op.ldc = p.K;
+            a = p.dy_codes + m0 * p.N; as = p.dy_scale + m0;
+            lda = p.N; ldas = p.m_total; rows_a = (int)min((int64_t)BWD_BM, off1 - m0);
+            b = p.wt_codes + k0 * p.Pw + cw; bs = p.wt_scale + (cw / 32) * p.K + k0;
+            ldb = p.Pw; ldbs = p.K; rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
+            R = p.N;
+            c = reinterpret_cast<char*>(p.out) + (m0 * p.K + k0) * esz; ldc = p.K;
         } else {
             // dW_e[n][k] = sum_{m in e} dY^T[n][m] X^T[k][m]
             const int KT = (int)((p.K + BWD_BN - 1) / BWD_BN);
             int nt, kt;
-            grouped_tile(local, (int)((p.N + BWD_BM - 1) / BWD_BM), KT, nt, kt);
+            grouped_tile(tr.local, (int)((p.N + BWD_BM - 1) / BWD_BM), KT, nt, kt);
             const int64_t n0 = (int64_t)nt * BWD_BM, k0 = (int64_t)kt * BWD_BN;
             const int64_t c0 = 32 * ((int64_t)e + off0 / 32);  // segment start column
-            op.a = p.dyt_codes + n0 * p.P + c0; op.as = p.dyt_scale + (c0 / 32) * p.N + n0;
-            op.lda = p.P; op.ldas = p.N; op.rows_a = (int)min((int64_t)BWD_BM, p.N - n0);
-            op.b = p.xt_codes + k0 * p.P + c0; op.bs = p.xt_scale + (c0 / 32) * p.K + k0;
-            op.ldb = p.P; op.ldbs = p.K; op.rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
-            op.R = 32 * ((off1 - off0 + 31) / 32);
-            op.c = reinterpret_cast<char*>(p.out) + (((int64_t)e * p.N + n0) * p.K + k0) * esz; op.ldc = p.K;
+            a = p.dyt_codes + n0 * p.P + c0; as = p.dyt_scale + (c0 / 32) * p.N + n0;
+            lda = p.P; ldas = p.N; rows_a = (int)min((int64_t)BWD_BM, p.N - n0);
+            b = p.xt_codes + k0 * p.P + c0; bs = p.xt_scale + (c0 / 32) * p.K + k0;
+            ldb = p.P; ldbs = p.K; rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
+            R = 32 * ((off1 - off0 + 31) / 32);
+            c = reinterpret_cast<char*>(p.out) + (((int64_t)e * p.N + n0) * p.K + k0) * esz; ldc = p.K;
         }
-        op.a = uniform_ptr(op.a); op.as = uniform_ptr(op.as);
-        op.b = uniform_ptr(op.b); op.bs = uniform_ptr(op.bs);
-        op.c = uniform_ptr(op.c);
-        op.lda = uniform_i64(op.lda); op.ldas = uniform_i64(op.ldas);
-        op.ldb = uniform_i64(op.ldb); op.ldbs = uniform_i64(op.ldbs);
-        op.ldc = uniform_i64(op.ldc); op.R = uniform_i64(op.R);
-        op.rows_a = __builtin_amdgcn_readfirstlane(op.rows_a);
-        op.rows_b = __builtin_amdgcn_readfirstlane(op.rows_b);
-        const int nsteps = (int)((op.R + 63) / 64);  // 64-byte MFMA k steps
-
-        const i32x4 dA = make_desc(op.a), dB = make_desc(op.b);
-        const i32x4 dAs = make_desc(op.as), dBs = make_desc(op.bs);
-        const uint32_t lda = (uint32_t)op.lda, ldb = (uint32_t)op.ldb;
-        const uint32_t ldas = (uint32_t)op.ldas, ldbs = (uint32_t)op.ldbs;
-        const uint32_t R = (uint32_t)op.R;
-
-        // Per-tile lane offsets at k = 0 (row part; the chunk is added per
-        // instruction); rows past the tile read as zero.
-        const uint32_t vra = (uint32_t)drow0 * lda, vrb = (uint32_t)drow0 * ldb;
-        // scales: instruction i (of 4) covers k block (4 * wave + i) >> 2 of
-        // the super-stage, rows 64 * ((4 * wave + i) & 3) + lane
-        uint32_t vsa[4], vsb[4];
+        BwdTile ts;
+        ts.dA = make_desc(uniform_ptr(a)); ts.dAs = make_desc(uniform_ptr(as));
+        ts.dB = make_desc(uniform_ptr(b)); ts.dBs = make_desc(uniform_ptr(bs));
+        ts.lda = __builtin_amdgcn_readfirstlane((uint32_t)lda);
+        ts.ldb = __builtin_amdgcn_readfirstlane((uint32_t)ldb);
+        ts.ldas = __builtin_amdgcn_readfirstlane((uint32_t)ldas);
+        ts.ldbs = __builtin_amdgcn_readfirstlane((uint32_t)ldbs);
+        ts.R = __builtin_amdgcn_readfirstlane((uint32_t)R);
+        ts.rows_a = __builtin_amdgcn_readfirstlane(rows_a);
+        ts.rows_b = __builtin_amdgcn_readfirstlane(rows_b);
+        ts.nsteps = (int)((ts.R + 63) / 64);  // 64-byte MFMA k steps
+        ts.c = uniform_ptr(c);
+        ts.ldcb = __builtin_amdgcn_readfirstlane((uint32_t)(ldc * esz));
+        // code instruction i (0..7) of this wave covers rows 64 * wave + 8i + lane / 8
+        const int drow0 = 64 * wave + (lane >> 3);
+        ts.vra = (uint32_t)drow0 * ts.lda;
+        ts.vrb = (uint32_t)drow0 * ts.ldb;
+        // scale instruction i (of 4) covers k block (4 * wave + i) >> 2 of the
+        // super-stage, rows 64 * ((4 * wave + i) & 3) + lane
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int ins = 4 * wave + i;
             const int row = 64 * (ins & 3) + lane;
             const uint32_t kb = (uint32_t)(ins >> 2);
-            vsa[i] = row < op.rows_a ? kb * ldas + row : OOB;
-            vsb[i] = row < op.rows_b ? kb * ldbs + row : OOB;
+            ts.vsa[i] = row < ts.rows_a ? kb * ts.ldas + row : OOB;
+            ts.vsb[i] = row < ts.rows_b ? kb * ts.ldbs + row : OOB;
         }
+        return ts;
+    };
 
-        // DMA of super-stage S into ring slot S % 2 (24 instructions per
-        // wave), in 12 parts of 2 so they can sit between MFMAs: parts 0..7
-        // move code rows (A and B of instruction i), parts 8..11 scale blocks.
-        // A 16-byte chunk or a 32-element scale block past R reads as zero.
-        auto issue_part = [&](int S, auto PC) {
-            constexpr int part = decltype(PC)::value;
-            const uint32_t q = (uint32_t)S & 1;
-            const uint32_t kbase = (uint32_t)S * SS_BK;
-            if constexpr (part < 8) {
-                constexpr int i = part;
-                const int row = drow0 + 8 * i;
-                const uint32_t ch = (i & 1) ? dch1 : dch0;
-                const bool okk = kbase + 16 * ch < R;
-                const uint32_t ko = kbase + 16 * ch;
-                const uint32_t slot = q * SS_TILE + 8192u * (uint32_t)wave;
-                dma16(dA, (okk & (row < op.rows_a)) ? vra + (uint32_t)(8 * i) * lda + ko : OOB,
-                      lds_at<1024u * i>(LA + slot));
-                dma16(dB, (okk & (row < op.rows_b)) ? vrb + (uint32_t)(8 * i) * ldb + ko : OOB,
-                      lds_at<1024u * i>(LB + slot));
-            } else {
-                constexpr int i = part - 8;
-                const int ins = 4 * wave + i;
-                const uint32_t blk = 4 * (uint32_t)S + (uint32_t)(ins >> 2);
-                const bool oks = blk * 32 < R;
-                const uint32_t sblk = 4 * (uint32_t)S;
-                const uint32_t slot = 4u * (q * 1024u + 256u * (uint32_t)wave);
-                dma1(dAs, oks ? vsa[i] + sblk * ldas : OOB, lds_at<256u * i>(LSA + slot));
-                dma1(dBs, oks ? vsb[i] + sblk * ldbs : OOB, lds_at<256u * i>(LSB + slot));
-            }
-        };
-        auto issue = [&](int S) {
-            issue_part(S, IC<0>{}); issue_part(S, IC<1>{}); issue_part(S, IC<2>{}); issue_part(S, IC<3>{});
-            issue_part(S, IC<4>{}); issue_part(S, IC<5>{}); issue_part(S, IC<6>{}); issue_part(S, IC<7>{});
-            issue_part(S, IC<8>{}); issue_part(S, IC<9>{}); issue_part(S, IC<10>{}); issue_part(S, IC<11>{});
-        };
+    // DMA of super-stage S of tile ts into ring slot S % 2 (24 instructions
+    // per wave), in 12 parts of 2 so they can sit between MFMAs: parts 0..7
+    // move code rows (A and B of instruction i), parts 8..11 scale blocks.
+    // The lane fetches logical chunk (lane & 7) ^ swz8(row) into slot
+    // lane & 7; swz8(row) depends on lane / 8 and the parity of i.  A 16-byte
+    // chunk or a 32-element scale block past R reads as zero.
+    auto issue_part = [&](const BwdTile& ts, int S, auto PC) {
+        constexpr int part = decltype(PC)::value;
+        const int lane = lane_of() & 63;
+        const uint32_t q = (uint32_t)S & 1;
+        const uint32_t kbase = (uint32_t)S * SS_BK;
+        if constexpr (part < 8) {
+            constexpr int i = part;
+            const int row = 64 * wave + 8 * i + (lane >> 3);
+            const uint32_t ch = (uint32_t)((lane & 7) ^ swz8(8 * (i & 1) + (lane >> 3)));
+            const bool okk = kbase + 16 * ch < ts.R;
+            const uint32_t ko = kbase + 16 * ch;
+            const uint32_t base = lds0 + q * SLOT_BYTES + 8192u * (uint32_t)wave;
+            dma16(ts.dA, (okk & (row < ts.rows_a)) ? ts.vra + (uint32_t)(8 * i) * ts.lda + ko : OOB,
+                  lds_at<offsetof(BwdSlot, a) + 1024u * i>(base));
+            dma16(ts.dB, (okk & (row < ts.rows_b)) ? ts.vrb + (uint32_t)(8 * i) * ts.ldb + ko : OOB,
+                  lds_at<offsetof(BwdSlot, b) + 1024u * i>(base));
+        } else {
+            constexpr int i = part - 8;
+            const int ins = 4 * wave + i;
+            const uint32_t blk = 4 * (uint32_t)S + (uint32_t)(ins >> 2);
+            const bool oks = blk * 32 < ts.R;
+            const uint32_t sblk = 4 * (uint32_t)S;
+            const uint32_t base = lds0 + q * SLOT_BYTES + 1024u * (uint32_t)wave;
+            dma1(ts.dAs, oks ? ts.vsa[i] + sblk * ts.ldas : OOB, lds_at<offsetof(BwdSlot, sa) + 256u * i>(base));
+            dma1(ts.dBs, oks ? ts.vsb[i] + sblk * ts.ldbs : OOB, lds_at<offsetof(BwdSlot, sb) + 256u * i>(base));
+        }
+    };
+    auto issue = [&](const BwdTile& ts, int S) {
+        issue_part(ts, S, IC<0>{}); issue_part(ts, S, IC<1>{}); issue_part(ts, S, IC<2>{});
+        issue_part(ts, S, IC<3>{}); issue_part(ts, S, IC<4>{}); issue_part(ts, S, IC<5>{});
+        issue_part(ts, S, IC<6>{}); issue_part(ts, S, IC<7>{}); issue_part(ts, S, IC<8>{});
+        issue_part(ts, S, IC<9>{}); issue_part(ts, S, IC<10>{}); issue_part(ts, S, IC<11>{});
+    };
+
+    {
+        const BwdTile first = setup(tile);
+        issue(first, 0);
+        issue(first, 1);
+    }
+
+    for (;;) {
+        // this tile's state, rebuilt from the LDS decode tables (not carried
+        // across iterations, which would force it through memory)
+        const BwdTile cur = setup(tile);
+        const int tid = lane_of();
+        const int lane = tid & 63;
+        const int lr = lane & 31, g = lane >> 5;
+        // Fragment read geometry: lane (lr, g) of k step h reads chunks 4h + g
+        // and 4h + g + 2 of row lr of each 32-row group; swz8(row) = swz8(lr),
+        // and (4h + g + 2d) ^ swz8 = (g ^ swz8) ^ (4h + 2d).
+        const uint32_t fr = (uint32_t)(lr * SS_BK + 16 * (g ^ swz8(lr)));
+        const uint32_t fa = offsetof(BwdSlot, a) + (uint32_t)(wm * 128 * SS_BK);
+        const uint32_t fb = offsetof(BwdSlot, b) + (uint32_t)(wn * 128 * SS_BK);
+        const uint32_t fsa = offsetof(BwdSlot, sa) + 4u * (uint32_t)(256 * g + wm * 128 + lr);
+        const uint32_t fsb = offsetof(BwdSlot, sb) + 4u * (uint32_t)(256 * g + wn * 128 + lr);
+
+        // claim the next tile now; the atomic's latency hides behind this one
+        int next_tile = 0;
+        if (tid == 0) next_tile = claim_tile(p.plan, xcd, total, dq);
+
         // Fragments of k step t (ring slot (t / 2) % 2, half h = t % 2): lane
         // (row, g) takes logical chunks 4h + g and 4h + g + 2 of its row (the
         // MFMA's k order) and the scale of block 2h + g.  Part 2i reads the A
@@ -234,8 +264,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         auto read_part = [&](int t, BwdFrag& f, int part) {
             const uint32_t q = ((uint32_t)t >> 1) & 1, h = (uint32_t)t & 1;
             const int i = part >> 1;
-            const uint32_t so = ((part & 1) ? fsb : fsa) + q * 4096u + h * 2048u + 128u * i;
-            const uint32_t o = ((part & 1) ? fb : fa) + q * SS_TILE + (uint32_t)(32 * i * SS_BK);
+            const uint32_t so = q * SLOT_BYTES + ((part & 1) ? fsb : fsa) + h * 2048u + 128u * i;
+            const uint32_t o = q * SLOT_BYTES + ((part & 1) ? fb : fa) + (uint32_t)(32 * i * SS_BK);
             const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + (fr ^ (64u * h)));
             const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + (fr ^ (64u * h + 32u)));
             const int sc = *(const __attribute__((address_space(3))) int*)(lds + so);
@@ -265,14 +295,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         };
         // k step t (fragments in cur) with t even: both halves of its
         // super-stage are in LDS; the MFMAs of t run with the reads of t+1.
-        auto step_even = [&](int t, const BwdFrag& cur, BwdFrag& nxt) {
+        auto step_even = [&](int t, const BwdFrag& cf, BwdFrag& nf) {
             wait_lgkmcnt0();
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const int i = k >> 2, j = k & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
-                                                                          cur.sa[i], 0, cur.sb[j]);
-                if (k >= 2 && k < 10) read_part(t + 1, nxt, k - 2);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cf.a[i], cf.b[j], acc[i][j], 0, 0, 0,
+                                                                          cf.sa[i], 0, cf.sb[j]);
+                if (k >= 2 && k < 10) read_part(t + 1, nf, k - 2);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -280,7 +310,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         // DMA in flight) and every wave holds both halves of super-stage t/2
         // in registers, then refill its slot with super-stage t/2 + 2 while
         // the MFMAs of t run, and read t+1.
-        auto step_odd = [&](int t, const BwdFrag& cur, BwdFrag& nxt) {
+        auto step_odd = [&](int t, const BwdFrag& cf, BwdFrag& nf) {
             wait_vmcnt<0>();
             wait_lgkmcnt0();
             block_barrier();
@@ -288,114 +318,123 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const int i = k >> 2, j = k & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
-                                                                          cur.sa[i], 0, cur.sb[j]);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cf.a[i], cf.b[j], acc[i][j], 0, 0, 0,
+                                                                          cf.sa[i], 0, cf.sb[j]);
                 switch (k) {
-                    case 0: issue_part(S, IC<0>{}); break;
-                    case 1: issue_part(S, IC<1>{}); break;
-                    case 2: issue_part(S, IC<2>{}); break;
-                    case 3: issue_part(S, IC<3>{}); break;
-                    case 4: issue_part(S, IC<4>{}); break;
-                    case 5: issue_part(S, IC<5>{}); break;
-                    case 6: issue_part(S, IC<6>{}); break;
-                    case 7: issue_part(S, IC<7>{}); break;
-                    case 8: issue_part(S, IC<8>{}); break;
-                    case 9: issue_part(S, IC<9>{}); break;
-                    case 10: issue_part(S, IC<10>{}); break;
-                    case 11: issue_part(S, IC<11>{}); break;
+                    case 0: issue_part(cur, S, IC<0>{}); break;
+                    case 1: issue_part(cur, S, IC<1>{}); break;
+                    case 2: issue_part(cur, S, IC<2>{}); break;
+                    case 3: issue_part(cur, S, IC<3>{}); break;
+                    case 4: issue_part(cur, S, IC<4>{}); break;
+                    case 5: issue_part(cur, S, IC<5>{}); break;
+                    case 6: issue_part(cur, S, IC<6>{}); break;
+                    case 7: issue_part(cur, S, IC<7>{}); break;
+                    case 8: issue_part(cur, S, IC<8>{}); break;
+                    case 9: issue_part(cur, S, IC<9>{}); break;
+                    case 10: issue_part(cur, S, IC<10>{}); break;
+                    case 11: issue_part(cur, S, IC<11>{}); break;
                     default: break;
                 }
-                if (k >= 4 && k < 12) read_part(t + 1, nxt, k - 4);
+                if (k >= 4 && k < 12) read_part(t + 1, nf, k - 4);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
 
-        // Prologue: super-stages 0 and 1 in flight, k step 0 read into X.
-        issue(0); issue(1);
-        wait_vmcnt<SS_DMA>();
+        // super-stages 0 and 1 are in flight (issued by the previous tile or
+        // the kernel prologue); wait for 0
+        wait_vmcnt<SS_DMA>();  // super-stage 1 may still fly
         block_barrier();
         BwdFrag X, Y;
         read(0, X);
         int t = 0;
-        for (; t + 1 < nsteps; t += 2) {
+        for (; t + 1 < cur.nsteps; t += 2) {
             step_even(t, X, Y);
             step_odd(t + 1, Y, X);
         }
-        if (t < nsteps) {
+        if (t < cur.nsteps) {
             wait_lgkmcnt0();
             mma(X);
         }
-        // drain every DMA of this tile before the ring is reused
+        // drain every DMA of this tile and publish the next tile
         wait_vmcnt<0>();
+        if (tid == 0) s_tile = next_tile;
         wait_lgkmcnt0();
         block_barrier();
+        tile = __builtin_amdgcn_readfirstlane(s_tile);
 
-        // Epilogue: the fp32 tile goes through the (now idle) LDS ring in two
-        // passes of 128 rows (each wave contributes its row groups i = 2p and
-        // 2p+1), then leaves as whole rows in 16-byte stores: f32 as is, bf16
-        // rounded to nearest even.  Lane (lr, g) holds column wn*128 + 32j + lr
-        // of rows wm*128 + 32i + 8(v/4) + 4g + v%4.  The staging pitch of 1056
-        // bytes puts the two lane halves (rows 4 apart) on disjoint banks.
-        // Stores outside a partial tile get an out-of-range offset.
+        // The next tile's first super-stage goes to slot 0 now, so its
+        // latency hides behind the epilogue, which stages through slot 1.
+        const int tnext = tile >= 0 ? tile : 0;  // a valid index for the unused case
+        const BwdTile nxt = setup(tnext);
+        if (tile >= 0) issue(nxt, 0);
+
+        // Epilogue: the fp32 tile goes through slot 1 in four passes of 64
+        // rows (pass i: every wave's row group i), then leaves as whole rows
+        // in 16-byte stores: f32 as is, bf16 rounded to nearest even.  Lane
+        // (lr, g) holds column wn*128 + 32j + lr of rows wm*128 + 32i +
+        // 8(v/4) + 4g + v%4.  Staged row r (0..63) = wm * 32 + (row % 32) keeps
+        // 1024 bytes; its 128-byte segments are swapped in pairs when bit 2 of
+        // r is set, which puts the two lane halves (rows 4 apart) on disjoint
+        // banks.  Stores outside a partial tile get an out-of-range offset.
         {
-            constexpr uint32_t EP = 1056;  // bytes per staged row (256 f32 + 32)
-            const __amdgpu_buffer_rsrc_t rc = make_rsrc(op.c, 0x7FFFFFFFu);
-            const uint32_t ldcb = (uint32_t)op.ldc * (uint32_t)esz;
-            __attribute__((address_space(3))) uint8_t* st = (__attribute__((address_space(3))) uint8_t*)(smem_raw);
-            const uint32_t wbase = (uint32_t)(wm * 64 + 4 * g) * EP + (uint32_t)(wn * 128 + lr) * 4u;
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(cur.c, 0x7FFFFFFFu);
+            __attribute__((address_space(3))) uint8_t* st =
+                (__attribute__((address_space(3))) uint8_t*)(smem_raw) + SLOT_BYTES;
+            const uint32_t wrow = (uint32_t)(wm * 32 + 4 * g) * 1024u + (uint32_t)(wn * 512 + 4 * lr);
+            const uint32_t wev = wrow + 128u * (uint32_t)g;        // column tiles j = 0, 2
+            const uint32_t wod = wrow + 128u * (uint32_t)(1 - g);  // column tiles j = 1, 3
 #pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
+            for (int pass = 0; pass < 4; ++pass) {
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int i = 2 * pass + ii;
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const uint32_t o = wbase + (uint32_t)(32 * ii + 8 * (v >> 2) + (v & 3)) * EP + 128u * j;
-                            *(__attribute__((address_space(3))) float*)(st + o) = acc[i][j][v];
-                        }
-                }
+                    for (int v = 0; v < 16; ++v) {
+                        const uint32_t o = ((j & 1) ? wod : wev) + 256u * (j >> 1) +
+                                           (uint32_t)(8 * (v >> 2) + (v & 3)) * 1024u;
+                        *(__attribute__((address_space(3))) float*)(st + o) = acc[pass][j][v];
+                    }
                 wait_lgkmcnt0();
                 block_barrier();
-                // staged row r (0..127) is tile row (r / 64) * 128 + 64 * pass + r % 64
                 if constexpr (OUT_F32) {
-#pragma unroll 4
-                    for (int it = 0; it < 32; ++it) {
-                        const int c = it * 256 + tid;          // 64 chunks of 16 bytes per row
+#pragma unroll
+                    for (int it = 0; it < 16; ++it) {
+                        const int c = it * 256 + tid;          // 64 chunks of 4 columns per row
                         const int r = c >> 6, cc = c & 63;
-                        const int row = (r >> 6) * 128 + 64 * pass + (r & 63);
-                        const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 16u * cc);
-                        const bool ok = (row < op.rows_a) & (4 * cc < op.rows_b);
-                        __builtin_amdgcn_raw_buffer_store_b128(x, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0, 0);
+                        const int row = (r >> 5) * 128 + 32 * pass + (r & 31);
+                        const uint32_t sw = 128u * (uint32_t)((r >> 2) & 1);
+                        const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * 1024u + ((16u * cc) ^ sw));
+                        const bool ok = (row < cur.rows_a) & (4 * cc < cur.rows_b);
+                        __builtin_amdgcn_raw_buffer_store_b128(x, rc, ok ? (int)((uint32_t)row * cur.ldcb + 16u * cc) : (int)OOB, 0, 0);
                     }
                 } else {
-#pragma unroll 4
-                    for (int it = 0; it < 16; ++it) {
+#pragma unroll
+                    for (int it = 0; it < 8; ++it) {
                         const int c = it * 256 + tid;          // 32 chunks of 8 bf16 per row
                         const int r = c >> 5, cc = c & 31;
-                        const int row = (r >> 6) * 128 + 64 * pass + (r & 63);
-                        const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 32u * cc);
-                        const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 32u * cc + 16u);
+                        const int row = (r >> 5) * 128 + 32 * pass + (r & 31);
+                        const uint32_t sw = 128u * (uint32_t)((r >> 2) & 1);
+                        const uint32_t ro = (uint32_t)r * 1024u;
+                        const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + ((32u * cc) ^ sw));
+                        const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + ((32u * cc + 16u) ^ sw));
                         u32x4 y;
                         y[0] = f32_to_bf16_rne(__uint_as_float(x0[0])) | (f32_to_bf16_rne(__uint_as_float(x0[1])) << 16);
                         y[1] = f32_to_bf16_rne(__uint_as_float(x0[2])) | (f32_to_bf16_rne(__uint_as_float(x0[3])) << 16);
                         y[2] = f32_to_bf16_rne(__uint_as_float(x1[0])) | (f32_to_bf16_rne(__uint_as_float(x1[1])) << 16);
                         y[3] = f32_to_bf16_rne(__uint_as_float(x1[2])) | (f32_to_bf16_rne(__uint_as_float(x1[3])) << 16);
-                        const bool ok = (row < op.rows_a) & (8 * cc < op.rows_b);
-                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0, 0);
+                        const bool ok = (row < cur.rows_a) & (8 * cc < cur.rows_b);
+                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * cur.ldcb + 16u * cc) : (int)OOB, 0, 0);
                     }
                 }
                 // every wave's reads of this pass are done before the next
-                // pass (or the next tile's DMA) overwrites the staging area;
-                // the last barrier also publishes the next tile
-                if (pass == 1 && tid == 0) s_tile = next_tile;
+                // pass (or the next tile's second super-stage) overwrites slot 1
                 wait_lgkmcnt0();
                 block_barrier();
             }
         }
-        tile = __builtin_amdgcn_readfirstlane(s_tile);
+        if (tile < 0) break;
+        issue(nxt, 1);
     }
+    // outstanding output stores complete before the wave ends
 }
 
 size_t bwd_smem_bytes() { return sizeof(BwdSmem); }
