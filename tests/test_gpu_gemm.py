@@ -154,22 +154,25 @@ def _sampled_rows(off, rng, first=4, last=4, rand=8):
     return out
 
 
+@pytest.mark.parametrize("cfg_id", [3, 5])
 @pytest.mark.parametrize("which", ["gate_up", "down"])
-def test_fwd_full_size_sampled(orc, bsq_gpu, which):
-    """Config 3 shapes at full size (32 experts, Zipf(1.1) over 32768 slots,
-    hidden 7168, intermediate 2048), launched exactly as the bench does; the
-    oracle checks sampled rows x sampled output channels of every expert."""
-    cfg = CONFIGS[3]
+def test_fwd_full_size_sampled(orc, bsq_gpu, which, cfg_id):
+    """Full-size forward shapes launched exactly as the bench does: config 3
+    (32 experts, Zipf(1.1) over 32768 slots) and config 5 (48 experts, 8 of
+    them empty, Zipf(1.5) over 65536 slots), hidden 7168, intermediate 2048.
+    The oracle checks sampled rows x sampled output channels of every
+    non-empty expert."""
+    cfg = CONFIGS[cfg_id]
     counts = moe_counts(cfg)
     off = offsets_from_counts(counts)
     E = cfg.n_experts
     n, k = (2 * cfg.inter, cfg.hidden) if which == "gate_up" else (cfg.hidden, cfg.inter)
-    gen = torch.Generator(device="cuda").manual_seed(3003 if which == "gate_up" else 3004)
+    gen = torch.Generator(device="cuda").manual_seed(1000 * cfg_id + (3 if which == "gate_up" else 4))
     x = torch.randn((cfg.m_total, k), generator=gen, device="cuda").to(torch.bfloat16)
     w = (torch.randn((E * n, k), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
     a_d, w_d = bsq_gpu.bsq_quantize_nvfp4v(x), bsq_gpu.bsq_quantize_nvfp4v(w)
     y = bsq_gpu.bsq_grouped_gemm_fwd(a_d, w_d, _to_dev(off), n, k, y_dtype=bsq_gpu.BSQ_F32)
-    rng = rng_for(3, salt=17)
+    rng = rng_for(cfg_id, salt=17)
     cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 30, replace=False)]))
     for e, rows in _sampled_rows(off, rng):
         xa = _bits(x[torch.from_numpy(rows).cuda()])
@@ -240,15 +243,18 @@ def test_bwd_deterministic(orc, bsq_gpu):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_bwd_full_size_sampled(orc, bsq_gpu):
-    """Config 4 (down projection: n = 7168, k = 2048) at full size: dgrad on
-    sampled rows of every expert; wgrad on sampled output rows of the two
-    smallest and the largest experts."""
-    cfg = CONFIGS[4]
+@pytest.mark.parametrize("cfg_id", [4, 5])
+def test_bwd_full_size_sampled(orc, bsq_gpu, cfg_id):
+    """Full-size backward of the down projection (n = 7168, k = 2048):
+    config 4 (32 experts, 32768 slots) and config 5 (48 experts with 8 empty,
+    65536 slots).  dgrad on sampled rows of every expert; wgrad on sampled
+    output rows of the two smallest non-empty and the largest experts; the
+    wgrad of an empty expert is all zeros."""
+    cfg = CONFIGS[cfg_id]
     counts = moe_counts(cfg)
     off = offsets_from_counts(counts)
     E, n, k, M = cfg.n_experts, cfg.hidden, cfg.inter, cfg.m_total
-    gen = torch.Generator(device="cuda").manual_seed(4004)
+    gen = torch.Generator(device="cuda").manual_seed(4004 + cfg_id)
     dy = (torch.randn((M, n), generator=gen, device="cuda") * 1e-3).to(torch.bfloat16)
     h = torch.randn((M, k), generator=gen, device="cuda").to(torch.bfloat16)
     w = (torch.randn((E * n, k), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
@@ -260,7 +266,7 @@ def test_bwd_full_size_sampled(orc, bsq_gpu):
     ht_d = bsq_gpu.bsq_quantize_mxfp8(h, bsq_gpu.BSQ_COLWISE_T, offsets=offd)
     dx, dw = bsq_gpu.bsq_grouped_gemm_bwd(offd, M, n, k, dy_d, wt_d, dyt_d, ht_d, dx_dtype=bsq_gpu.BSQ_F32,
                                           dw_dtype=bsq_gpu.BSQ_F32)
-    rng = rng_for(4, salt=19)
+    rng = rng_for(cfg_id, salt=19)
     kcols = np.unique(np.concatenate([[0, k - 1], rng.choice(k, 30, replace=False)]))
     for e, rows in _sampled_rows(off, rng, 2, 2, 4):
         dy_q = orc.quantize_mxfp8_rowwise(_bits(dy[torch.from_numpy(rows).cuda()]))
@@ -271,9 +277,11 @@ def test_bwd_full_size_sampled(orc, bsq_gpu):
         absum = orc.grouped_gemm_dgrad(dy_q, wt_q, seg, n, absolute=True)
         got = _np(dx[torch.from_numpy(rows).cuda()][:, torch.from_numpy(kcols).cuda()]).astype(np.float64)
         check_groups(got, ref, [(("dgrad", e), np.arange(len(rows)))], strict=False, absum=absum)
-    order = np.argsort(counts, kind="stable")
+    order = [int(e) for e in np.argsort(counts, kind="stable") if counts[e] > 0]
     nrows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 14, replace=False)]))
-    for e in [int(order[0]), int(order[1]), int(order[-1])]:
+    for e in np.nonzero(np.asarray(counts) == 0)[0][:1]:
+        assert not bool(dw[int(e)].any())
+    for e in [order[0], order[1], order[-1]]:
         m0, m1 = int(off[e]), int(off[e + 1])
         seg = np.array([0, m1 - m0], np.int32)
         dyt_q = orc.quantize_mxfp8_colwise_t(_bits(dy[m0:m1][:, torch.from_numpy(nrows).cuda()]), seg)

@@ -150,6 +150,20 @@ def test_nvfp4v_batch_invariance_gpu(bsq_gpu):
             assert np.array_equal(f[sel].view(np.uint8), _np(p).view(np.uint8))
 
 
+def test_mxfp8_rowwise_batch_invariance_gpu(bsq_gpu):
+    """MXFP8 row-wise codes and scale bytes of a row do not depend on the
+    batch it is quantized in (shuffled batches of random sizes)."""
+    rng = rng_for(5, salt=4)
+    x = make_quantize_input(rng, 1024, 7168)
+    xd = _bf16_dev(x)
+    fc, fs = [_np(t) for t in bsq_gpu.bsq_quantize_mxfp8(xd, bsq_gpu.BSQ_ROWWISE)]
+    for _ in range(16):
+        n = int(rng.integers(1, 1024))
+        sel = rng.permutation(1024)[:n]
+        pc, ps = bsq_gpu.bsq_quantize_mxfp8(xd[torch.from_numpy(sel).cuda()].contiguous(), bsq_gpu.BSQ_ROWWISE)
+        assert np.array_equal(fc[sel], _np(pc)) and np.array_equal(fs[:, sel], _np(ps))
+
+
 def test_nvfp4v_strided_input(orc, bsq_gpu):
     rng = rng_for(2, salt=5)
     big = make_quantize_input(rng, 40, 512)
