@@ -45,14 +45,23 @@ def parse():
 
 
 def copy_mode():
+    """1 GiB device-to-device copy, three launches: the calibration kernel for
+    the FETCH_SIZE / WRITE_SIZE counters, and the practical HBM ceiling of a
+    read-write stream (timed with HIP events)."""
     import torch
     n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst.copy_(src)
+    a.record()
     for _ in range(3):
         dst.copy_(src)
+    b.record()
     torch.cuda.synchronize()
-    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+    ms = a.elapsed_time(b) / 3
+    print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "launches": 4,
+                      "ms_per_copy": round(ms, 4), "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
 def main():
@@ -216,6 +225,8 @@ def main():
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 1), "peak": dom_peak,
                 "unit": "TFLOP/s", "frac": round(dom_tf / dom_peak, 4), "traffic": traffic.get(dom)}
 
+    quant = quantize_config2(bsq, torch, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, counts, off_np)
@@ -233,8 +244,49 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "quantize": quant,
     }
     print(json.dumps(out))
+
+
+def quantize_config2(bsq, torch, dev, reps=20):
+    """Quantize-only workload: 16384 tokens x 7168 hidden bf16 ~N(0,1) with
+    1% (72) outlier channels scaled x50.  Algorithmic bytes: bf16 read plus
+    codes and scales written; HIP events on the launch stream."""
+    R, C = 16384, 7168
+    gen = torch.Generator(device=dev).manual_seed(2002)
+    x = torch.randn((R, C), generator=gen, device=dev)
+    cols = torch.randperm(C, generator=gen, device=dev)[:72]
+    x[:, cols] *= 50.0
+    x = x.to(torch.bfloat16)
+    one = torch.tensor([0, R], dtype=torch.int32, device=dev)
+    nv = (torch.empty((R, C // 2), dtype=torch.uint8, device=dev), torch.empty((R, C // 16), dtype=torch.uint8, device=dev),
+          torch.empty((R,), dtype=torch.float32, device=dev))
+    mr = (torch.empty((R, C), dtype=torch.uint8, device=dev), torch.empty((C // 32, R), dtype=torch.uint8, device=dev))
+    P = bsq.bsq_colwise_padded_cols(1, R)
+    mc = (torch.empty((C, P), dtype=torch.uint8, device=dev), torch.empty((P // 32, C), dtype=torch.uint8, device=dev))
+    cases = {
+        "nvfp4v": (lambda: bsq.bsq_quantize_nvfp4v(x, *nv), 2 * R * C + R * C // 2 + R * C // 16 + 4 * R),
+        "mxfp8_rowwise": (lambda: bsq.bsq_quantize_mxfp8(x, bsq.BSQ_ROWWISE, codes=mr[0], scale=mr[1]),
+                          2 * R * C + R * C + R * C // 32),
+        "mxfp8_colwise_t": (lambda: bsq.bsq_quantize_mxfp8(x, bsq.BSQ_COLWISE_T, offsets=one, codes=mc[0], scale=mc[1]),
+                            2 * R * C + C * P + C * P // 32),
+    }
+    stream = torch.cuda.current_stream()
+    out = {"workload": "quantize: 16384 x 7168 bf16 N(0,1), 72 outlier channels x50"}
+    for name, (fn, nbytes) in cases.items():
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 2), "bytes": nbytes, "gbps": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_GBS, 4)}
+    return out
 
 
 def kernel_source_hash(stage):

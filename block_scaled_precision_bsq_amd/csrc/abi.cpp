@@ -102,6 +102,7 @@ bsq_status bsq_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t cols, in
         if (rows == 0 || cols == 0) return BSQ_OK;
         if (!x_bf16 || ld_x < cols) return BSQ_ERR_INVALID_ARG;
         if (cols % 32 || ld_x % 8 || !aligned(x_bf16, 16) || !aligned(codes, 16)) return BSQ_ERR_UNSUPPORTED;
+        if (256 * ld_x >= kMaxBufferOffset) return BSQ_ERR_UNSUPPORTED;  // 32-bit offsets within a 128-row tile
         return from_hip(bsq::launch_quantize_mxfp8_rowwise(static_cast<const uint16_t*>(x_bf16), rows, (int)cols,
                                                            ld_x, codes, scale, stream));
     }

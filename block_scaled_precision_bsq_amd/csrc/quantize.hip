@@ -186,23 +186,37 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* 
     const int t = threadIdx.x;
     const int bl = t & 31;       // block within the tile
     const int b = b0 + bl;
-#pragma unroll 4
-    for (int it = 0; it < MXR_ROWS / 8; ++it) {
-        const int rl = 8 * it + (t >> 5);
-        const int64_t row = r0 + rl;
-        if (row < rows && b < nb) {
-            const uint4* p = reinterpret_cast<const uint4*>(x + row * ldx + 32 * b);
-            uint32_t w[16];
+    // Row offsets are relative to the tile's first row: 128 * ldx * 2 bytes
+    // stay below 2^31 (host check).  Rows past the end and blocks past the
+    // row read as zero and are not stored.
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(x + r0 * ldx), 0x7FFFFFFFu);
+    const bool okb = b < nb;
+#pragma unroll 1
+    for (int it = 0; it < MXR_ROWS / 8; it += 4) {
+        // four rows of this thread's block in flight at once
+        uint32_t w[4][16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int rl = 8 * (it + u) + (t >> 5);
+            const bool ok = okb & (r0 + rl < rows);
+            const uint32_t off = (uint32_t)(((int64_t)rl * ldx + 32 * b) * 2);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint4 v = ld_stream16(p + q);
-                w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+                const uint4 v = buf_load16(rx, ok ? off + 16u * q : OOB);
+                w[u][4 * q] = v.x; w[u][4 * q + 1] = v.y; w[u][4 * q + 2] = v.z; w[u][4 * q + 3] = v.w;
             }
-            const MxBlock r = mx_encode(w);
-            uint4* o = reinterpret_cast<uint4*>(codes + row * (int64_t)cols + 32 * b);
-            o[0] = r.c0;
-            o[1] = r.c1;
-            sb[bl * MXR_PITCH + rl] = (uint8_t)r.sbyte;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int rl = 8 * (it + u) + (t >> 5);
+            const int64_t row = r0 + rl;
+            const MxBlock r = mx_encode(w[u]);
+            if (okb & (row < rows)) {
+                uint4* o = reinterpret_cast<uint4*>(codes + row * (int64_t)cols + 32 * b);
+                o[0] = r.c0;
+                o[1] = r.c1;
+                sb[bl * MXR_PITCH + rl] = (uint8_t)r.sbyte;
+            }
         }
     }
     __syncthreads();
@@ -274,8 +288,10 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
     const int c_base = (int)(blockIdx.x % nct) * COLT_CH;
 
     if (wave == 0) {
-        // groups of the 4 blocks lie within g0 .. g0 + 3 (a group spans >= 32 columns)
-        const int g0 = __builtin_amdgcn_readfirstlane(colt_find_base(offsets, ngroups, p0, lane));
+        // groups of the 4 blocks lie within g0 .. g0 + 3 (a group spans >= 32
+        // columns); with at most 61 groups the window starting at group 0
+        // holds them all and one round of loads does
+        const int g0 = ngroups <= 61 ? 0 : __builtin_amdgcn_readfirstlane(colt_find_base(offsets, ngroups, p0, lane));
         const int g = g0 + lane;
         const bool have = g < ngroups;
         const int32_t of0 = have ? offsets[g] : 0;
