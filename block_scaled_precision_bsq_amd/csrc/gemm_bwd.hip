@@ -43,7 +43,6 @@ constexpr int BWD_BM = 256;
 constexpr int BWD_BN = 256;
 constexpr int SS_BK = 128;                       // bytes of k per row per super-stage
 constexpr int SS_TILE = PIPE_ROWS * SS_BK;       // one operand's super-stage (32 KB)
-constexpr int SS_DMA = 24;                       // DMA instructions per wave per super-stage
 
 // One ring slot: codes of both operands and their scale bytes (one dword per
 // (k block, row): block * 256 + row).  Slot-major so that a whole slot is
@@ -52,8 +51,8 @@ constexpr int SS_DMA = 24;                       // DMA instructions per wave pe
 struct BwdSlot {
     uint8_t a[SS_TILE];
     uint8_t b[SS_TILE];
-    uint32_t sa[4 * PIPE_ROWS];
-    uint32_t sb[4 * PIPE_ROWS];
+    uint32_t sa[4 * PIPE_ROWS];  // dgrad: one dword per (block, row); wgrad: packed bytes [block][row]
+    uint8_t sb[4 * PIPE_ROWS];   // packed bytes [block][row]
 };
 struct BwdSmem {
     BwdSlot slot[2];
@@ -82,11 +81,16 @@ struct BwdTile {
     char* c;
     uint32_t ldcb;
     uint32_t vra, vrb;
-    uint32_t vsa[4], vsb[4];
+    uint32_t vsa[4];  // dgrad A scale rows (one byte per lane)
 };
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool WGRAD>
 __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
+    // DMA instructions per wave per super-stage: 16 code rows, the A scales
+    // (four 64-byte pieces of block-major bytes for dgrad, whose token rows
+    // start anywhere; one packed 256-byte block for wgrad, whose rows start
+    // at a multiple of 256) and one packed 256-byte block of B scales.
+    constexpr int SS_DMA = WGRAD ? 18 : 21;
     extern __shared__ __align__(16) uint8_t smem_raw[];
     __shared__ int s_tile;
 
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         int64_t lda, ldas, ldb, ldbs, R, ldc;
         int rows_a, rows_b;
         char* c;
-        if (!p.wgrad) {
+        if constexpr (!WGRAD) {
             // dX[m][k] = sum_n dY[m][n] Wt_e[k][n]
             const int KT = (int)((p.K + BWD_BN - 1) / BWD_BN);
             int mt, kt;
@@ -186,7 +190,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             const int row = 64 * (ins & 3) + lane;
             const uint32_t kb = (uint32_t)(ins >> 2);
             ts.vsa[i] = row < ts.rows_a ? kb * ts.ldas + row : OOB;
-            ts.vsb[i] = row < ts.rows_b ? kb * ts.ldbs + row : OOB;
         }
         return ts;
     };
@@ -213,15 +216,34 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                   lds_at<offsetof(BwdSlot, a) + 1024u * i>(base));
             dma16(ts.dB, (okk & (row < ts.rows_b)) ? ts.vrb + (uint32_t)(8 * i) * ts.ldb + ko : OOB,
                   lds_at<offsetof(BwdSlot, b) + 1024u * i>(base));
+        } else if constexpr (part < 12) {
+            // dgrad A scales: instruction i covers k block (4 * wave + i) >> 2 of
+            // the super-stage, rows 64 * ((4 * wave + i) & 3) + lane, one
+            // dword per byte
+            if constexpr (!WGRAD) {
+                constexpr int i = part - 8;
+                const int ins = 4 * wave + i;
+                const uint32_t blk = 4 * (uint32_t)S + (uint32_t)(ins >> 2);
+                const bool oks = blk * 32 < ts.R;
+                const uint32_t sblk = 4 * (uint32_t)S;
+                const uint32_t base = lds0 + q * SLOT_BYTES + 1024u * (uint32_t)wave;
+                dma1(ts.dAs, oks ? ts.vsa[i] + sblk * ts.ldas : OOB, lds_at<offsetof(BwdSlot, sa) + 256u * i>(base));
+            }
         } else {
-            constexpr int i = part - 8;
-            const int ins = 4 * wave + i;
-            const uint32_t blk = 4 * (uint32_t)S + (uint32_t)(ins >> 2);
+            // Packed scale blocks: wave w moves block w of the super-stage for
+            // A (wgrad) and B as 16 lanes x 16 bytes; rows past the tile and
+            // blocks past R read as zero, the other 48 lanes are switched off.
+            const uint32_t blk = 4 * (uint32_t)S + (uint32_t)wave;
             const bool oks = blk * 32 < ts.R;
-            const uint32_t sblk = 4 * (uint32_t)S;
-            const uint32_t base = lds0 + q * SLOT_BYTES + 1024u * (uint32_t)wave;
-            dma1(ts.dAs, oks ? ts.vsa[i] + sblk * ts.ldas : OOB, lds_at<offsetof(BwdSlot, sa) + 256u * i>(base));
-            dma1(ts.dBs, oks ? ts.vsb[i] + sblk * ts.ldbs : OOB, lds_at<offsetof(BwdSlot, sb) + 256u * i>(base));
+            const uint32_t rb = 16u * (uint32_t)(lane & 15);
+            const uint32_t base = lds0 + q * SLOT_BYTES + 256u * (uint32_t)wave;
+            if (lane < 16) {
+                if constexpr (WGRAD)
+                    dma16(ts.dAs, (oks & (rb < (uint32_t)ts.rows_a)) ? blk * ts.ldas + rb : OOB,
+                          lds_at<offsetof(BwdSlot, sa)>(base));
+                dma16(ts.dBs, (oks & (rb < (uint32_t)ts.rows_b)) ? blk * ts.ldbs + rb : OOB,
+                      lds_at<offsetof(BwdSlot, sb)>(base));
+            }
         }
     };
     auto issue = [&](const BwdTile& ts, int S) {
@@ -229,6 +251,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         issue_part(ts, S, IC<3>{}); issue_part(ts, S, IC<4>{}); issue_part(ts, S, IC<5>{});
         issue_part(ts, S, IC<6>{}); issue_part(ts, S, IC<7>{}); issue_part(ts, S, IC<8>{});
         issue_part(ts, S, IC<9>{}); issue_part(ts, S, IC<10>{}); issue_part(ts, S, IC<11>{});
+        issue_part(ts, S, IC<12>{});
     };
 
     {
@@ -250,8 +273,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         const uint32_t fr = (uint32_t)(lr * SS_BK + 16 * (g ^ swz8(lr)));
         const uint32_t fa = offsetof(BwdSlot, a) + (uint32_t)(wm * 128 * SS_BK);
         const uint32_t fb = offsetof(BwdSlot, b) + (uint32_t)(wn * 128 * SS_BK);
-        const uint32_t fsa = offsetof(BwdSlot, sa) + 4u * (uint32_t)(256 * g + wm * 128 + lr);
-        const uint32_t fsb = offsetof(BwdSlot, sb) + 4u * (uint32_t)(256 * g + wn * 128 + lr);
+        // scale of (block 2h + g, row): dword block * 256 + row (dgrad A) or
+        // byte block * 256 + row (packed)
+        constexpr uint32_t ESA = WGRAD ? 1u : 4u;
+        const uint32_t fsa = offsetof(BwdSlot, sa) + ESA * (uint32_t)(256 * g + wm * 128 + lr);
+        const uint32_t fsb = offsetof(BwdSlot, sb) + (uint32_t)(256 * g + wn * 128 + lr);
 
         // claim the next tile now; the atomic's latency hides behind this one
         int next_tile = 0;
@@ -264,11 +290,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         auto read_part = [&](int t, BwdFrag& f, int part) {
             const uint32_t q = ((uint32_t)t >> 1) & 1, h = (uint32_t)t & 1;
             const int i = part >> 1;
-            const uint32_t so = q * SLOT_BYTES + ((part & 1) ? fsb : fsa) + h * 2048u + 128u * i;
+            const uint32_t es = (part & 1) ? 1u : ESA;
+            const uint32_t so = q * SLOT_BYTES + ((part & 1) ? fsb : fsa) + es * (h * 512u + 32u * i);
             const uint32_t o = q * SLOT_BYTES + ((part & 1) ? fb : fa) + (uint32_t)(32 * i * SS_BK);
             const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + (fr ^ (64u * h)));
             const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + (fr ^ (64u * h + 32u)));
-            const int sc = *(const __attribute__((address_space(3))) int*)(lds + so);
+            const int sc = (es == 4u) ? *(const __attribute__((address_space(3))) int*)(lds + so)
+                                      : (int)*(const __attribute__((address_space(3))) uint8_t*)(lds + so);
             const int8v v = int8v{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
             if (part & 1) { f.b[i] = v; f.sb[i] = sc; } else { f.a[i] = v; f.sa[i] = sc; }
         };
@@ -333,6 +361,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                     case 9: issue_part(cur, S, IC<9>{}); break;
                     case 10: issue_part(cur, S, IC<10>{}); break;
                     case 11: issue_part(cur, S, IC<11>{}); break;
+                    case 12: issue_part(cur, S, IC<12>{}); break;
                     default: break;
                 }
                 if (k >= 4 && k < 12) read_part(t + 1, nf, k - 4);
@@ -450,22 +479,30 @@ hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s) {
     }
     if (err != hipSuccess) return err;
     static bool attr_set = false;  // idempotent; racing writers set the same value
+    const int lds_max = (int)(sizeof(BwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E));
     if (!attr_set) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)(sizeof(BwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
-        if (err != hipSuccess) return err;
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)(sizeof(BwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
-        if (err != hipSuccess) return err;
+        const void* ks[4] = {reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, true>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, true>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false>)};
+        for (const void* k : ks) {
+            err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
+            if (err != hipSuccess) return err;
+        }
         attr_set = true;
     }
     const size_t lds = sizeof(BwdSmem) + lds_table_bytes(args.E);
-    if (args.out_f32)
-        hipLaunchKernelGGL(k_gemm_bwd_mxfp8<true>, dim3(grid), dim3(256), lds, s, args);
-    else
-        hipLaunchKernelGGL(k_gemm_bwd_mxfp8<false>, dim3(grid), dim3(256), lds, s, args);
+    if (args.out_f32) {
+        if (args.wgrad)
+            hipLaunchKernelGGL((k_gemm_bwd_mxfp8<true, true>), dim3(grid), dim3(256), lds, s, args);
+        else
+            hipLaunchKernelGGL((k_gemm_bwd_mxfp8<true, false>), dim3(grid), dim3(256), lds, s, args);
+    } else {
+        if (args.wgrad)
+            hipLaunchKernelGGL((k_gemm_bwd_mxfp8<false, true>), dim3(grid), dim3(256), lds, s, args);
+        else
+            hipLaunchKernelGGL((k_gemm_bwd_mxfp8<false, false>), dim3(grid), dim3(256), lds, s, args);
+    }
     return hipGetLastError();
 }
 
