@@ -326,12 +326,16 @@ def measured_traffic():
 
 
 def cpu_baseline(cfg, counts, off_np):
-    """The oracle as it stands, on a bounded sample: NVFP4-variant quantize +
-    float64 forward gate/up GEMM for the first rows of a few experts."""
+    """The oracle as it stands, on a bounded sample of the same step: for one
+    expert at a time, largest first, every quantization and all six GEMMs of
+    the step (forward gate/up, SwiGLU, forward down, dgrad and wgrad of both
+    projections) on that expert's rows, until about ``budget_s`` seconds of
+    oracle time are spent.  Rate = the GEMM flops of the experts done / the
+    oracle time (quantization included, input generation not)."""
     import numpy as np
 
     import oracle
-    from workloads import normal_bf16, rng_for
+    from workloads import f32_to_bf16_bits, normal_bf16, rng_for
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -339,28 +343,43 @@ def cpu_baseline(cfg, counts, off_np):
         blas_threads = os.cpu_count() or 1
     rng = rng_for(3, salt=55)
     Hd, I = cfg.hidden, cfg.inter
-    rows_per = 8192
-    budget_s = 15.0  # the sample stops at the first expert that ends past this
+    budget_s = 20.0  # the sample stops after the first expert that ends past this
     flops = 0.0
     done = []
     t_all = 0.0
     for e in [int(e) for e in np.argsort(-np.asarray(counts), kind="stable")]:
-        m = min(rows_per, int(counts[e]))
+        m = int(counts[e])
         if m == 0:
             break
-        x, w = normal_bf16(rng, (m, Hd)), normal_bf16(rng, (2 * I, Hd), 0.02)
+        x, dy = normal_bf16(rng, (m, Hd)), normal_bf16(rng, (m, Hd), 1e-3)
+        dgu = normal_bf16(rng, (m, 2 * I), 1e-3)
+        w_gu, w_d = normal_bf16(rng, (2 * I, Hd), 0.02), normal_bf16(rng, (Hd, I), 0.02)
+        seg = np.array([0, m], np.int32)
         t0 = time.perf_counter()
-        a_q, w_q = oracle.quantize_nvfp4v(x), oracle.quantize_nvfp4v(w)
-        oracle.grouped_gemm_fwd(a_q, w_q, np.array([0, m], np.int32))
+        # forward: NVFP4-variant operands
+        gu = oracle.grouped_gemm_fwd(oracle.quantize_nvfp4v(x), oracle.quantize_nvfp4v(w_gu), seg)
+        h = f32_to_bf16_bits(oracle.swiglu(gu).astype(np.float32))
+        oracle.grouped_gemm_fwd(oracle.quantize_nvfp4v(h), oracle.quantize_nvfp4v(w_d), seg)
+        # backward of the down projection: MXFP8 operands
+        oracle.grouped_gemm_dgrad(oracle.quantize_mxfp8_rowwise(dy),
+                                  oracle.quantize_mxfp8_colwise_t(w_d, np.array([0, Hd], np.int32)), seg, Hd)
+        oracle.grouped_gemm_wgrad(oracle.quantize_mxfp8_colwise_t(dy, seg),
+                                  oracle.quantize_mxfp8_colwise_t(h, seg), seg)
+        # backward of the gate/up projection
+        oracle.grouped_gemm_dgrad(oracle.quantize_mxfp8_rowwise(dgu),
+                                  oracle.quantize_mxfp8_colwise_t(w_gu, np.array([0, 2 * I], np.int32)), seg, 2 * I)
+        oracle.grouped_gemm_wgrad(oracle.quantize_mxfp8_colwise_t(dgu, seg),
+                                  oracle.quantize_mxfp8_colwise_t(x, seg), seg)
         t_all += time.perf_counter() - t0
-        flops += 2.0 * m * 2 * I * Hd
+        flops += 3 * 2.0 * m * (2 * I * Hd + Hd * I)
         done.append(m)
         if t_all >= budget_s:
             break
     return {"value": round(flops / t_all / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"NVFP4-variant quantize (activations and the expert's weights) + float64 gate/up GEMM "
-                      f"(n=4096, k=7168) over the first <= {rows_per} token-slots of the {len(done)} largest experts "
-                      f"({sum(done)} rows); stops after ~{budget_s:.0f} s; seconds={t_all:.1f}"}
+            "sample": f"the whole step (NVFP4-variant and MXFP8 quantizations, SwiGLU, float64 forward, dgrad and "
+                      f"wgrad GEMMs of both projections) for the {len(done)} largest of {len(counts)} experts "
+                      f"({sum(done)} of {int(np.sum(counts))} token-slots); stops after ~{budget_s:.0f} s; "
+                      f"seconds={t_all:.1f}"}
 
 
 if __name__ == "__main__":
