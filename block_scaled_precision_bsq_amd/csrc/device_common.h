@@ -37,10 +37,13 @@ __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t m, uint32_t w) {
     return max(m, max(lo, hi));
 }
 
-// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two floats -> packed bf16 pair, a in the low half, rounded to nearest even
+// by the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // E2M1 codes of two floats into nibbles of byte `sel` of `old`: low nibble

@@ -58,6 +58,9 @@ struct BwdSmem {
     BwdSlot slot[2];
 };
 constexpr uint32_t SLOT_BYTES = sizeof(BwdSlot);
+static_assert(SLOT_BYTES >= 128 * 512, "a bf16 epilogue pass stages 128 rows of 512 bytes in one slot");
+
+
 
 // One output tile of C[i][j] = sum_r A[i][r] B[j][r].
 struct TileOps {
@@ -397,34 +400,34 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         const BwdTile nxt = setup(tnext);
         if (tile >= 0) issue(nxt, 0);
 
-        // Epilogue: the fp32 tile goes through slot 1 in four passes of 64
-        // rows (pass i: every wave's row group i), then leaves as whole rows
-        // in 16-byte stores: f32 as is, bf16 rounded to nearest even.  Lane
-        // (lr, g) holds column wn*128 + 32j + lr of rows wm*128 + 32i +
-        // 8(v/4) + 4g + v%4.  Staged row r (0..63) = wm * 32 + (row % 32) keeps
-        // 1024 bytes; its 128-byte segments are swapped in pairs when bit 2 of
-        // r is set, which puts the two lane halves (rows 4 apart) on disjoint
-        // banks.  Stores outside a partial tile get an out-of-range offset.
+        // Epilogue through slot 1.  Lane (lr, g) holds column wn*128 + 32j + lr
+        // of rows wm*128 + 32i + 8(v/4) + 4g + v%4.  Stores outside a partial
+        // tile get an out-of-range offset.
         {
             const __amdgpu_buffer_rsrc_t rc = make_rsrc(cur.c, 0x7FFFFFFFu);
             __attribute__((address_space(3))) uint8_t* st =
                 (__attribute__((address_space(3))) uint8_t*)(smem_raw) + SLOT_BYTES;
-            const uint32_t wrow = (uint32_t)(wm * 32 + 4 * g) * 1024u + (uint32_t)(wn * 512 + 4 * lr);
-            const uint32_t wev = wrow + 128u * (uint32_t)g;        // column tiles j = 0, 2
-            const uint32_t wod = wrow + 128u * (uint32_t)(1 - g);  // column tiles j = 1, 3
+            if constexpr (OUT_F32) {
+                // f32: four passes of 64 rows (pass i: every wave's row group
+                // i), staged row r = wm * 32 + (row % 32) keeps 1024 bytes; its
+                // 128-byte segments are swapped in pairs when bit 2 of r is
+                // set, which puts the two lane halves (rows 4 apart) on
+                // disjoint banks.
+                const uint32_t wrow = (uint32_t)(wm * 32 + 4 * g) * 1024u + (uint32_t)(wn * 512 + 4 * lr);
+                const uint32_t wev = wrow + 128u * (uint32_t)g;        // column tiles j = 0, 2
+                const uint32_t wod = wrow + 128u * (uint32_t)(1 - g);  // column tiles j = 1, 3
 #pragma unroll
-            for (int pass = 0; pass < 4; ++pass) {
+                for (int pass = 0; pass < 4; ++pass) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const uint32_t o = ((j & 1) ? wod : wev) + 256u * (j >> 1) +
-                                           (uint32_t)(8 * (v >> 2) + (v & 3)) * 1024u;
-                        *(__attribute__((address_space(3))) float*)(st + o) = acc[pass][j][v];
-                    }
-                wait_lgkmcnt0();
-                block_barrier();
-                if constexpr (OUT_F32) {
+                        for (int v = 0; v < 16; ++v) {
+                            const uint32_t o = ((j & 1) ? wod : wev) + 256u * (j >> 1) +
+                                               (uint32_t)(8 * (v >> 2) + (v & 3)) * 1024u;
+                            *(__attribute__((address_space(3))) float*)(st + o) = acc[pass][j][v];
+                        }
+                    wait_lgkmcnt0();
+                    block_barrier();
 #pragma unroll
                     for (int it = 0; it < 16; ++it) {
                         const int c = it * 256 + tid;          // 64 chunks of 4 columns per row
@@ -433,31 +436,74 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                         const uint32_t sw = 128u * (uint32_t)((r >> 2) & 1);
                         const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * 1024u + ((16u * cc) ^ sw));
                         const bool ok = (row < cur.rows_a) & (4 * cc < cur.rows_b);
-                        __builtin_amdgcn_raw_buffer_store_b128(x, rc, ok ? (int)((uint32_t)row * cur.ldcb + 16u * cc) : (int)OOB, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(x, rc, ok ? (int)((uint32_t)row * cur.ldcb + 16u * cc) : (int)OOB, 0,
+                                                               OUT_STORE_NT);
                     }
-                } else {
+                    // every wave's reads of this pass are done before the next
+                    // pass (or the next tile's second super-stage) overwrites slot 1
+                    wait_lgkmcnt0();
+                    block_barrier();
+                }
+            } else {
+                // bf16: two passes of 128 rows (pass p: every wave's row
+                // groups 2p and 2p+1).  A lane rounds each pair of vertically
+                // adjacent values (v, v+1 with v even) into one dword, low half
+                // the even row, so LDS holds rows in pairs: pair P (64 per
+                // pass) keeps 1024 bytes, columns 8k..8k+3 of every 8-column
+                // chunk k in its first 512 bytes and columns 8k+4..8k+7 in the
+                // second.  The 64-byte units of each half are XOR-permuted by
+                // s = half + 2 * bit 1 of P, so the four 64-byte pieces one
+                // write instruction touches (two halves, pairs 2 apart) fall
+                // on different banks, while a read of 16 consecutive bytes per
+                // lane stays conflict-free.  Each read item (pair, chunk) then
+                // leaves as two 16-byte row stores.
+#pragma unroll
+                for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int v = 0; v < 16; v += 2) {
+                                const int P = wm * 32 + 16 * ii + 4 * (v >> 2) + 2 * g + ((v >> 1) & 1);
+                                const int col = wn * 128 + 32 * j + lr;
+                                const int k = col >> 3, w = col & 7, half = w >> 2;
+                                const uint32_t sx = 64u * (uint32_t)((half + 2 * ((P >> 1) & 1)) & 3);
+                                const uint32_t o = (uint32_t)P * 1024u + 512u * (uint32_t)half +
+                                                   ((16u * (uint32_t)k + 4u * (uint32_t)(w & 3)) ^ sx);
+                                *(__attribute__((address_space(3))) uint32_t*)(st + o) =
+                                    pack_bf16x2(acc[2 * pass + ii][j][v], acc[2 * pass + ii][j][v + 1]);
+                            }
+                    wait_lgkmcnt0();
+                    block_barrier();
 #pragma unroll
                     for (int it = 0; it < 8; ++it) {
-                        const int c = it * 256 + tid;          // 32 chunks of 8 bf16 per row
-                        const int r = c >> 5, cc = c & 31;
-                        const int row = (r >> 5) * 128 + 32 * pass + (r & 31);
-                        const uint32_t sw = 128u * (uint32_t)((r >> 2) & 1);
-                        const uint32_t ro = (uint32_t)r * 1024u;
-                        const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + ((32u * cc) ^ sw));
-                        const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + ((32u * cc + 16u) ^ sw));
-                        u32x4 y;
-                        y[0] = f32_to_bf16_rne(__uint_as_float(x0[0])) | (f32_to_bf16_rne(__uint_as_float(x0[1])) << 16);
-                        y[1] = f32_to_bf16_rne(__uint_as_float(x0[2])) | (f32_to_bf16_rne(__uint_as_float(x0[3])) << 16);
-                        y[2] = f32_to_bf16_rne(__uint_as_float(x1[0])) | (f32_to_bf16_rne(__uint_as_float(x1[1])) << 16);
-                        y[3] = f32_to_bf16_rne(__uint_as_float(x1[2])) | (f32_to_bf16_rne(__uint_as_float(x1[3])) << 16);
-                        const bool ok = (row < cur.rows_a) & (8 * cc < cur.rows_b);
-                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * cur.ldcb + 16u * cc) : (int)OOB, 0, 0);
+                        const int item = it * 256 + tid;
+                        const int P = item >> 5, k = item & 31;
+                        const uint32_t sa0 = 64u * (uint32_t)(2 * ((P >> 1) & 1));
+                        const uint32_t po = (uint32_t)P * 1024u;
+                        const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(st + po + ((16u * k) ^ sa0));
+                        const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(st + po + 512u + ((16u * k) ^ (sa0 + 64u)));
+                        u32x4 ev, od;
+                        ev[0] = __builtin_amdgcn_perm(x0[1], x0[0], 0x05040100u);
+                        ev[1] = __builtin_amdgcn_perm(x0[3], x0[2], 0x05040100u);
+                        ev[2] = __builtin_amdgcn_perm(x1[1], x1[0], 0x05040100u);
+                        ev[3] = __builtin_amdgcn_perm(x1[3], x1[2], 0x05040100u);
+                        od[0] = __builtin_amdgcn_perm(x0[1], x0[0], 0x07060302u);
+                        od[1] = __builtin_amdgcn_perm(x0[3], x0[2], 0x07060302u);
+                        od[2] = __builtin_amdgcn_perm(x1[1], x1[0], 0x07060302u);
+                        od[3] = __builtin_amdgcn_perm(x1[3], x1[2], 0x07060302u);
+                        const int row = (P >> 5) * 128 + 32 * (2 * pass + ((P >> 4) & 1)) + 2 * (P & 15);
+                        const bool okc = 8 * k < cur.rows_b;
+                        const uint32_t go = (uint32_t)row * cur.ldcb + 16u * (uint32_t)k;
+                        __builtin_amdgcn_raw_buffer_store_b128(ev, rc, (okc & (row < cur.rows_a)) ? (int)go : (int)OOB, 0, OUT_STORE_NT);
+                        __builtin_amdgcn_raw_buffer_store_b128(od, rc, (okc & (row + 1 < cur.rows_a)) ? (int)(go + cur.ldcb) : (int)OOB, 0, OUT_STORE_NT);
                     }
+                    // every wave's reads of this pass are done before the next
+                    // pass (or the next tile's second super-stage) overwrites slot 1
+                    wait_lgkmcnt0();
+                    block_barrier();
                 }
-                // every wave's reads of this pass are done before the next
-                // pass (or the next tile's second super-stage) overwrites slot 1
-                wait_lgkmcnt0();
-                block_barrier();
             }
         }
         if (tile < 0) break;

@@ -133,6 +133,11 @@ __device__ __forceinline__ TileRef decode_tile_any(bool in_lds, const __attribut
     return decode_tile<const int32_t*>(plan_start(plan), plan_order(plan, E), offsets, E, t);
 }
 
+// Cache policy of the GEMM output stores: non-temporal.  An output tile is
+// written once and never read back by the kernel, so it should not displace
+// operand panels from L2.
+constexpr int OUT_STORE_NT = 2;
+
 // Arguments of the MXFP8 backward GEMM kernel (one launch computes either the
 // dgrad or the wgrad tiles).
 struct BwdArgs {

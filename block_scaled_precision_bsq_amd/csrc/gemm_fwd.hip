@@ -339,7 +339,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
 #pragma unroll
                         for (int q = 0; q < 4; ++q) y[q] = __float_as_uint((__uint_as_float(x[q]) * sa) * rsw[4 * cc + q]);
                         const bool ok = (row < rows_a) & (4 * cc < rows_b);
-                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0,
+                                                               OUT_STORE_NT);
                     }
                 } else {
 #pragma unroll 4
@@ -358,9 +359,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
                         }
                         u32x4 y;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) y[q] = f32_to_bf16_rne(v[2 * q]) | (f32_to_bf16_rne(v[2 * q + 1]) << 16);
+                        for (int q = 0; q < 4; ++q) y[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
                         const bool ok = (row < rows_a) & (8 * cc < rows_b);
-                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0,
+                                                               OUT_STORE_NT);
                     }
                 }
                 // every wave's reads of this pass are done before the next
