@@ -5,7 +5,7 @@ One step = the whole hot path over one batch of the 32-expert shard
 popularity), inputs resident in HBM:
   forward  : NVFP4-variant quantize of W_gu, W_down (once per weight version,
              i.e. every optimizer step) and of X; gate/up grouped GEMM;
-             SwiGLU (harness, torch); quantize H; down grouped GEMM;
+             SwiGLU (harness activation) fused with the quantization of H; down grouped GEMM;
   backward : MXFP8 quantize of dY (row-wise and per-expert transposed), of the
              weights (transposed) and of H, dGU, X (transposed); dgrad and
              wgrad grouped GEMMs of the down and the gate/up projections.
@@ -76,9 +76,8 @@ def main():
     import numpy as np
     import torch
 
-    from block_scaled_precision_bsq_amd.build import LIB
-    if not os.path.exists(LIB):
-        from block_scaled_precision_bsq_amd.build import build
+    if not os.path.exists(os.path.join(ROOT, "block_scaled_precision_bsq_amd", "libbsq.so")):
+        from __graft_entry__ import build
         build()
     import block_scaled_precision_bsq_amd as bsq
     from workloads import CONFIGS, moe_counts, offsets_from_counts
@@ -138,8 +137,9 @@ def main():
         ("quant_nvfp4v_weights", lambda: (bsq.bsq_quantize_nvfp4v(w_gu, *q_wgu), bsq.bsq_quantize_nvfp4v(w_dn, *q_wdn))),
         ("quant_nvfp4v_x", lambda: bsq.bsq_quantize_nvfp4v(x, *q_x)),
         ("gemm_fwd_gate_up", lambda: bsq.bsq_grouped_gemm_fwd(q_x, q_wgu, off, 2 * I, Hd, y=gu, workspace=ws_f)),
-        ("swiglu", None),
-        ("quant_nvfp4v_h", lambda: bsq.bsq_quantize_nvfp4v(h, *q_h)),
+        # harness activation H = silu(gate) * up, fused with H's NVFP4v quantization
+        ("swiglu_quant_nvfp4v_h", lambda: bsq.bsq_swiglu_quantize_nvfp4v(gu, h=h, codes=q_h[0], bscale=q_h[1],
+                                                                          rscale=q_h[2])),
         ("gemm_fwd_down", lambda: bsq.bsq_grouped_gemm_fwd(q_h, q_wdn, off, Hd, I, y=y, workspace=ws_f)),
         ("quant_mxfp8_rowwise", lambda: (bsq.bsq_quantize_mxfp8(dy, R, codes=q_dy[0], scale=q_dy[1]),
                                          bsq.bsq_quantize_mxfp8(dgu, R, codes=q_dgu[0], scale=q_dgu[1]))),
@@ -160,10 +160,6 @@ def main():
                                                                     flags=bsq.BSQ_WGRAD, dw=dw_gu, workspace=ws_b)),
     ]
 
-    def swiglu_into():  # harness activation between the GEMMs: H = silu(gate) * up
-        h.copy_(torch.nn.functional.silu(gu[:, :I].float()).mul_(gu[:, I:].float()))
-    stages[3] = ("swiglu", swiglu_into)
-
     flops = {
         "gemm_fwd_gate_up": 2.0 * M * 2 * I * Hd, "gemm_fwd_down": 2.0 * M * Hd * I,
         "gemm_bwd_dgrad_down": 2.0 * M * Hd * I, "gemm_bwd_wgrad_down": 2.0 * M * Hd * I,
@@ -173,7 +169,7 @@ def main():
     mxb = lambda r, c: 2 * r * c + r * c + r * c // 32                       # bf16 in + codes + scales
     qbytes = {
         "quant_nvfp4v_weights": nvb(E * 2 * I, Hd) + nvb(E * Hd, I), "quant_nvfp4v_x": nvb(M, Hd),
-        "quant_nvfp4v_h": nvb(M, I), "quant_mxfp8_rowwise": mxb(M, Hd) + mxb(M, 2 * I),
+        "swiglu_quant_nvfp4v_h": 2 * M * 2 * I + nvb(M, I), "quant_mxfp8_rowwise": mxb(M, Hd) + mxb(M, 2 * I),
         "quant_mxfp8_colwise_t": mxb(E * Hd, I) + mxb(E * 2 * I, Hd) + mxb(M, Hd) + mxb(M, I) + mxb(M, 2 * I)
         + mxb(M, Hd),
     }
@@ -335,7 +331,7 @@ def cpu_baseline(cfg, counts, off_np):
     import numpy as np
 
     import oracle
-    from workloads import f32_to_bf16_bits, normal_bf16, rng_for
+    from workloads import normal_bf16, rng_for
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -358,7 +354,7 @@ def cpu_baseline(cfg, counts, off_np):
         t0 = time.perf_counter()
         # forward: NVFP4-variant operands
         gu = oracle.grouped_gemm_fwd(oracle.quantize_nvfp4v(x), oracle.quantize_nvfp4v(w_gu), seg)
-        h = f32_to_bf16_bits(oracle.swiglu(gu).astype(np.float32))
+        h = oracle.round_bf16(oracle.swiglu(gu))
         oracle.grouped_gemm_fwd(oracle.quantize_nvfp4v(h), oracle.quantize_nvfp4v(w_d), seg)
         # backward of the down projection: MXFP8 operands
         oracle.grouped_gemm_dgrad(oracle.quantize_mxfp8_rowwise(dy),

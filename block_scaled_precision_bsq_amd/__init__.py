@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbsq.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_scaled_precision_bsq_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python block_scaled_precision_bsq_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -35,6 +35,7 @@ BSQ_OP_GEMM_FWD, BSQ_OP_GEMM_BWD = 0, 1
 
 _SIGS = {
     "bsq_quantize_nvfp4v": ([P, I64, I64, I64, P, I32, P, P, P, P], INT),
+    "bsq_swiglu_quantize_nvfp4v": ([P, I64, I64, I64, P, I64, P, P, P, P], INT),
     "bsq_quantize_mxfp8": ([P, I64, I64, I64, INT, P, I32, P, P, P], INT),
     "bsq_grouped_gemm_fwd": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_bwd": ([P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, INT, ctypes.c_uint, P,
@@ -123,6 +124,37 @@ def bsq_quantize_nvfp4v(x, codes=None, bscale=None, rscale=None, offsets=None, s
            _lib.bsq_quantize_nvfp4v(_ptr(x), rows, cols, ld, _ptr(offsets), ng, _ptr(codes), _ptr(bscale),
                                     _ptr(rscale), _stream(stream)))
     return codes, bscale, rscale
+
+
+def bsq_swiglu_quantize_nvfp4v(gu, h=None, write_h=True, codes=None, bscale=None, rscale=None, stream=None):
+    """SwiGLU of bf16 ``gu`` [rows, 2*inter] ([gate | up] per row) fused with the
+    NVFP4-variant quantization of H = bf16(silu(gate) * up).
+    Returns (h bf16 [rows, inter] or None, codes u8 [rows, inter/2],
+    bscale u8 [rows, inter/16], rscale f32 [rows])."""
+    _dev(gu, "gu", _BF16)
+    rows, cols2, ld = _rows_ld(gu)
+    if cols2 % 2:
+        raise ValueError("gu must have an even number of columns ([gate | up])")
+    inter = cols2 // 2
+    dev = gu.device
+    if write_h and h is None:
+        h = torch.empty((rows, inter), dtype=torch.bfloat16, device=dev)
+    if h is not None:
+        _dev(h, "h", _BF16)
+        if tuple(h.shape) != (rows, inter) or (rows > 1 and h.stride(1) != 1):
+            raise ValueError(f"h must be row-major with shape {(rows, inter)}")
+    ldh = 0 if h is None else (h.stride(0) if rows > 1 else inter)
+    codes = torch.empty((rows, inter // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    bscale = torch.empty((rows, inter // 16), dtype=torch.uint8, device=dev) if bscale is None else bscale
+    rscale = torch.empty((rows,), dtype=torch.float32, device=dev) if rscale is None else rscale
+    for t, nm, shape in ((codes, "codes", (rows, inter // 2)), (bscale, "bscale", (rows, inter // 16)),
+                         (rscale, "rscale", (rows,))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous with shape {shape}")
+    _check("bsq_swiglu_quantize_nvfp4v",
+           _lib.bsq_swiglu_quantize_nvfp4v(_ptr(gu), rows, inter, ld, _ptr(h), ldh, _ptr(codes), _ptr(bscale),
+                                           _ptr(rscale), _stream(stream)))
+    return h, codes, bscale, rscale
 
 
 def bsq_quantize_mxfp8(x, axis=BSQ_ROWWISE, offsets=None, codes=None, scale=None, stream=None):

@@ -1,6 +1,6 @@
 """Build libbsq.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-``python -m block_scaled_precision_bsq_amd.build`` or ``build()`` compiles every
+``python block_scaled_precision_bsq_amd/build.py`` or ``build()`` compiles every
 source under ``csrc/`` into ``_build/`` (at the repository root) and links
 ``block_scaled_precision_bsq_amd/libbsq.so``.  No GPU is needed.
 """

@@ -12,6 +12,8 @@
 
 namespace bsq {
 hipError_t launch_quantize_nvfp4v(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, float*, hipStream_t);
+hipError_t launch_swiglu_quantize_nvfp4v(const uint16_t*, int64_t, int, int64_t, uint16_t*, int64_t, uint8_t*, uint8_t*,
+                                         float*, hipStream_t);
 hipError_t launch_quantize_mxfp8_rowwise(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, hipStream_t);
 hipError_t launch_quantize_mxfp8_colwise_t(const uint16_t*, int64_t, int, int64_t, const int32_t*, int, int64_t,
                                            uint8_t*, uint8_t*, hipStream_t);
@@ -87,6 +89,23 @@ bsq_status bsq_quantize_nvfp4v(const void* x_bf16, int64_t rows, int64_t cols, i
     if (rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
     return from_hip(bsq::launch_quantize_nvfp4v(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x, codes,
                                                 bscale, rscale, stream));
+}
+
+bsq_status bsq_swiglu_quantize_nvfp4v(const void* gu_bf16, int64_t rows, int64_t inter, int64_t ld_gu, void* h_bf16,
+                                      int64_t ld_h, uint8_t* codes, uint8_t* bscale, float* rscale,
+                                      hipStream_t stream) {
+    if (rows < 0 || inter < 0) return BSQ_ERR_INVALID_ARG;
+    if (rows == 0 || inter == 0) return BSQ_OK;
+    if (!gu_bf16 || !codes || !bscale || !rscale || ld_gu < 2 * inter) return BSQ_ERR_INVALID_ARG;
+    if (h_bf16 && ld_h < inter) return BSQ_ERR_INVALID_ARG;
+    if (inter % 16 || inter > 16384 || ld_gu % 8 || !aligned(gu_bf16, 16) || !aligned(codes, 8) ||
+        !aligned(rscale, 4))
+        return BSQ_ERR_UNSUPPORTED;
+    if (h_bf16 && (ld_h % 8 || !aligned(h_bf16, 16))) return BSQ_ERR_UNSUPPORTED;
+    if (rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
+    return from_hip(bsq::launch_swiglu_quantize_nvfp4v(static_cast<const uint16_t*>(gu_bf16), rows, (int)inter, ld_gu,
+                                                       static_cast<uint16_t*>(h_bf16), ld_h, codes, bscale, rscale,
+                                                       stream));
 }
 
 bsq_status bsq_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x, bsq_axis axis,

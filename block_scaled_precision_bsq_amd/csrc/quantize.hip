@@ -32,11 +32,31 @@ namespace bsq {
 // a binary32 rounding midpoint and lies at least 2^-49 (relative) away from
 // every midpoint, so both round to the same binary32 number.  The reciprocal
 // costs one binary64 division per 16 elements instead of 16 fp32 divisions.
-template <int BPL>
+//
+// SWIGLU: x holds rows [gate | up] of 2 * cols bf16 and the row quantized is
+// H = bf16_RNE(silu(gate) * up) (the activation between the two forward
+// GEMMs; it is not on the pages).  silu(g) = g * sigmoid(g) is evaluated in
+// binary32 from t = e^-|g|, which never overflows: g / (1 + t) for g >= 0 and
+// (g * t) / (1 + t) for g < 0, so a very negative gate gives the tiny value it
+// should instead of g / inf.  H is also written to h (when non-null), so the
+// backward pass can quantize the same values; the quantization of H is the
+// one above, byte for byte.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float t = expf(-fabsf(g));
+    const float num = g >= 0.0f ? g : g * t;
+    return (num / (1.0f + t)) * u;
+}
+
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
+    return pack_bf16x2(silu_mul(bf16_lo(gw), bf16_lo(uw)), silu_mul(bf16_hi(gw), bf16_hi(uw)));
+}
+
+template <int BPL, bool SWIGLU>
 __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restrict__ x, int64_t rows,
                                                          int cols, int64_t ldx, uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ bscale,
-                                                         float* __restrict__ rscale) {
+                                                         float* __restrict__ rscale, uint16_t* __restrict__ h,
+                                                         int64_t ldh) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
@@ -53,6 +73,19 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restr
             const uint4* p = reinterpret_cast<const uint4*>(xr + 16 * b);
             v[i][0] = ld_stream16(p);
             v[i][1] = ld_stream16(p + 1);
+            if constexpr (SWIGLU) {
+                const uint4* pu = reinterpret_cast<const uint4*>(xr + cols + 16 * b);
+                const uint4 u0 = ld_stream16(pu), u1 = ld_stream16(pu + 1);
+                v[i][0] = make_uint4(swiglu_pair(v[i][0].x, u0.x), swiglu_pair(v[i][0].y, u0.y),
+                                     swiglu_pair(v[i][0].z, u0.z), swiglu_pair(v[i][0].w, u0.w));
+                v[i][1] = make_uint4(swiglu_pair(v[i][1].x, u1.x), swiglu_pair(v[i][1].y, u1.y),
+                                     swiglu_pair(v[i][1].z, u1.z), swiglu_pair(v[i][1].w, u1.w));
+                if (h) {
+                    uint4* ph = reinterpret_cast<uint4*>(h + row * ldh + 16 * b);
+                    ph[0] = v[i][0];
+                    ph[1] = v[i][1];
+                }
+            }
         } else {
             v[i][0] = make_uint4(0, 0, 0, 0);
             v[i][1] = make_uint4(0, 0, 0, 0);
@@ -379,23 +412,39 @@ __global__ void k_debug_e4m3(const float* __restrict__ in, uint8_t* __restrict__
 
 // ---------------------------------------------------------------- launchers
 
-hipError_t launch_quantize_nvfp4v(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
-                                  uint8_t* bscale, float* rscale, hipStream_t s) {
+template <bool SWIGLU>
+static hipError_t launch_nvfp4v(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
+                                uint8_t* bscale, float* rscale, uint16_t* h, int64_t ldh, hipStream_t s) {
     const int nb = cols / 16;
     const dim3 grid((unsigned)((rows + 3) / 4));
+#define BSQ_NVFP4V_LAUNCH(BPL)                                                                                \
+    hipLaunchKernelGGL((k_quantize_nvfp4v<BPL, SWIGLU>), grid, dim3(256), 0, s, x, rows, cols, ldx, codes, \
+                       bscale, rscale, h, ldh)
     if (nb <= 64)
-        hipLaunchKernelGGL(k_quantize_nvfp4v<1>, grid, dim3(256), 0, s, x, rows, cols, ldx, codes, bscale, rscale);
+        BSQ_NVFP4V_LAUNCH(1);
     else if (nb <= 128)
-        hipLaunchKernelGGL(k_quantize_nvfp4v<2>, grid, dim3(256), 0, s, x, rows, cols, ldx, codes, bscale, rscale);
+        BSQ_NVFP4V_LAUNCH(2);
     else if (nb <= 256)
-        hipLaunchKernelGGL(k_quantize_nvfp4v<4>, grid, dim3(256), 0, s, x, rows, cols, ldx, codes, bscale, rscale);
+        BSQ_NVFP4V_LAUNCH(4);
     else if (nb <= 512)
-        hipLaunchKernelGGL(k_quantize_nvfp4v<8>, grid, dim3(256), 0, s, x, rows, cols, ldx, codes, bscale, rscale);
+        BSQ_NVFP4V_LAUNCH(8);
     else if (nb <= 1024)
-        hipLaunchKernelGGL(k_quantize_nvfp4v<16>, grid, dim3(256), 0, s, x, rows, cols, ldx, codes, bscale, rscale);
+        BSQ_NVFP4V_LAUNCH(16);
     else
         return hipErrorInvalidValue;  // rejected by the host checks (cols > 16384)
+#undef BSQ_NVFP4V_LAUNCH
     return hipGetLastError();
+}
+
+hipError_t launch_quantize_nvfp4v(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
+                                  uint8_t* bscale, float* rscale, hipStream_t s) {
+    return launch_nvfp4v<false>(x, rows, cols, ldx, codes, bscale, rscale, nullptr, 0, s);
+}
+
+hipError_t launch_swiglu_quantize_nvfp4v(const uint16_t* gu, int64_t rows, int inter, int64_t ldgu, uint16_t* h,
+                                         int64_t ldh, uint8_t* codes, uint8_t* bscale, float* rscale,
+                                         hipStream_t s) {
+    return launch_nvfp4v<true>(gu, rows, inter, ldgu, codes, bscale, rscale, h, ldh, s);
 }
 
 hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,

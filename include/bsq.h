@@ -66,7 +66,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define BSQ_ABI_VERSION 1
+#define BSQ_ABI_VERSION 2
 
 typedef enum {
     BSQ_OK = 0,
@@ -110,6 +110,31 @@ typedef enum {
 bsq_status bsq_quantize_nvfp4v(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                                const int32_t* offsets, int32_t num_groups,
                                uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t stream);
+
+/*
+ * bsq_swiglu_quantize_nvfp4v -- the activation between the two forward
+ * expert GEMMs fused with the NVFP4-variant quantization of its output, so
+ * the down projection's input is quantized without another pass over H
+ * ("Composer 2 Technical Report", section 6.1: NVFP4 variant on the MoE
+ * forward activations; the per-token absmax is fused into the quantizer as
+ * in "Cursor Composer 2 report deep dive", section 1).  The activation itself
+ * is not on the pages; this library takes SwiGLU: for each row of
+ * [gate | up] (2 * inter bf16), H[c] = bf16_RNE(silu(g) * u), g = row[c],
+ * u = row[inter + c], with silu evaluated in binary32 from t = e^-|g|:
+ * g / (1 + t) for g >= 0, (g * t) / (1 + t) for g < 0 (IEEE division, expf).  H is then quantized exactly as
+ * bsq_quantize_nvfp4v quantizes a bf16 row (same bytes).
+ *   gu_bf16 [rows][ld_gu] bf16, 16-byte aligned, ld_gu % 8 == 0,
+ *   ld_gu >= 2 * inter; inter % 16 == 0, inter <= 16384.
+ *   h_bf16 [rows][ld_h] (optional, may be NULL): receives H; 16-byte aligned,
+ *   ld_h % 8 == 0, ld_h >= inter.
+ *   codes [rows][inter/2], bscale [rows][inter/16], rscale [rows]: outputs.
+ * Row-local, batch invariant.  rows == 0 or inter == 0: nothing to do.
+ * Errors: INVALID_ARG (null pointers, negative sizes, short leading
+ *   dimensions), UNSUPPORTED (inter multiple or size, alignment), HIP.
+ */
+bsq_status bsq_swiglu_quantize_nvfp4v(const void* gu_bf16, int64_t rows, int64_t inter, int64_t ld_gu,
+                                      void* h_bf16, int64_t ld_h,
+                                      uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t stream);
 
 /*
  * bsq_quantize_mxfp8 -- MXFP8 quantization ("Composer 2 Technical Report",

@@ -293,6 +293,35 @@ def grouped_gemm_wgrad(dyt_q, xt_q, offsets, experts=None, absolute=False) -> di
 
 def swiglu(gu: np.ndarray) -> np.ndarray:
     """Harness activation between the two forward GEMMs (not on the pages):
-    [gate | up] along the last axis, H = silu(gate) * up, in float64."""
+    [gate | up] along the last axis, H = silu(gate) * up, in float64, with
+    silu(g) = g / (1 + e^-g) written as g e^g / (1 + e^g) for g < 0 so that
+    no exponential overflows."""
     g, u = np.split(np.asarray(gu, np.float64), 2, axis=-1)
-    return g / (1.0 + np.exp(-g)) * u
+    t = np.exp(-np.abs(g))
+    return np.where(g >= 0, g, g * t) / (1.0 + t) * u
+
+
+def round_bf16(x) -> np.ndarray:
+    """float64 -> bf16 bit patterns (uint16), one rounding to nearest even.
+
+    bf16 keeps 8 significant bits, exponents down to -126 (normal) and a
+    subnormal quantum of 2**-133; magnitudes at or beyond the halfway point
+    above the largest finite value become infinity.  NaN is not handled.
+    """
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    m, e = np.frexp(a)                      # a = m * 2**e, m in [0.5, 1)
+    e = np.maximum(e, -125)                 # below 2**-126 the quantum stops shrinking
+    q = np.ldexp(1.0, e - 8)                # quantum of the 8-significant-bit grid
+    r = np.rint(a / q) * q                  # a / q and the product are exact in float64
+    r = np.where(r >= 2.0 ** 128, np.inf, r)
+    bits = (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # r is a bf16 value
+    return np.where(np.signbit(x), bits | np.uint16(0x8000), bits).astype(np.uint16)
+
+
+def swiglu_bf16(gu_bf16: np.ndarray) -> np.ndarray:
+    """H = silu(gate) * up of bf16 [gate | up] rows, computed in float64 and
+    rounded once to bf16 (bit patterns)."""
+    g = _bf16(gu_bf16)
+    f = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return round_bf16(swiglu(f))

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(bsq):
 
 
 def test_version_and_helpers(bsq):
-    assert bsq.ABI_VERSION == 1
+    assert bsq.ABI_VERSION == 2
     assert bsq.bsq_colwise_padded_cols(32, 32768) == 32 * (32 + 1024)
     assert bsq.bsq_colwise_padded_cols(3, 0) == 96
     assert bsq.bsq_colwise_padded_cols(2, 33) == 32 * (2 + 2)
