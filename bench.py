@@ -222,6 +222,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(dom_tf / dom_peak, 4), "traffic": traffic.get(dom)}
 
     quant = quantize_config2(bsq, torch, dev)
+    fwd_mx = fwd_mxfp8_compare(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M,
+                               {k: stage_ms[k] for k in ("gemm_fwd_gate_up", "gemm_fwd_down")}, ws_f)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -241,6 +243,7 @@ def main():
         "cpu_baseline": cpu,
         "breakdown": breakdown,
         "quantize": quant,
+        "fwd_mxfp8": fwd_mx,
     }
     print(json.dumps(out))
 
@@ -282,6 +285,41 @@ def quantize_config2(bsq, torch, dev, reps=20):
         us = a.elapsed_time(b) * 1e3 / reps
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 2), "bytes": nbytes, "gbps": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_GBS, 4)}
+    return out
+
+
+def fwd_mxfp8_compare(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, nv_ms, ws, reps=10):
+    """The forward expert GEMMs again with all-MXFP8 operands (ROWWISE X, H and
+    weights; block-scaled fp8 MFMA) on the same tensors, outside the step:
+    the MXFP8 alternative to the NVFP4-variant forward.  HIP events on the
+    launch stream; quantization not timed."""
+    R = bsq.BSQ_ROWWISE
+    q = {"x": bsq.bsq_quantize_mxfp8(x, R), "w_gu": bsq.bsq_quantize_mxfp8(w_gu, R),
+         "h": bsq.bsq_quantize_mxfp8(h, R), "w_dn": bsq.bsq_quantize_mxfp8(w_dn, R)}
+    y_gu = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    y_dn = torch.empty((M, Hd), dtype=torch.bfloat16, device=dev)
+    cases = {
+        "gemm_fwd_gate_up": (lambda: bsq.bsq_grouped_gemm_fwd_mxfp8(q["x"], q["w_gu"], off, 2 * I, Hd, y=y_gu,
+                                                                    workspace=ws), 2.0 * M * 2 * I * Hd),
+        "gemm_fwd_down": (lambda: bsq.bsq_grouped_gemm_fwd_mxfp8(q["h"], q["w_dn"], off, Hd, I, y=y_dn,
+                                                                 workspace=ws), 2.0 * M * Hd * I),
+    }
+    stream = torch.cuda.current_stream()
+    out = {"operands": "MXFP8 ROWWISE activations and weights, block-scaled fp8 MFMA, bf16 out"}
+    for name, (fn, fl) in cases.items():
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK["fp8"], 4),
+                     "speedup_vs_nvfp4v_fwd": round(nv_ms[name] / ms, 3)}
+    del q, y_gu, y_dn
     return out
 
 

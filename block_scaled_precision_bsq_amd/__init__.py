@@ -40,6 +40,7 @@ _SIGS = {
     "bsq_grouped_gemm_fwd": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_bwd": ([P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, INT, ctypes.c_uint, P,
                               ctypes.c_size_t, P], INT),
+    "bsq_grouped_gemm_fwd_mxfp8": ([P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
     "bsq_workspace_size": ([INT, I32, I64, I64, I64], ctypes.c_size_t),
     "bsq_colwise_padded_cols": ([I32, I64], I64),
     "bsq_status_string": ([INT], ctypes.c_char_p),
@@ -213,6 +214,28 @@ def bsq_grouped_gemm_fwd(a_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, work
                                      _ptr(w_rscale), _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype,
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+    return y
+
+
+def bsq_grouped_gemm_fwd_mxfp8(x_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, workspace=None, stream=None):
+    """Forward grouped GEMM over MXFP8 operands.  x_q / w_q = ROWWISE (codes,
+    scale) of the expert-sorted activations [m_total, k] and of the weights
+    [E*n, k] (block-major scales)."""
+    x_codes, x_scale = x_q
+    w_codes, w_scale = w_q
+    _dev(offsets, "offsets", (torch.int32,))
+    E = offsets.numel() - 1
+    m_total = x_codes.shape[0]
+    if w_codes.shape[0] != E * n:
+        raise ValueError("weights must hold num_experts * n rows")
+    dev = x_codes.device
+    if y is None:
+        y = torch.empty((m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev)
+    _check("bsq_grouped_gemm_fwd_mxfp8",
+           _lib.bsq_grouped_gemm_fwd_mxfp8(_ptr(x_codes), _ptr(x_scale), _ptr(w_codes), _ptr(w_scale),
+                                           _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype, _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
 
 

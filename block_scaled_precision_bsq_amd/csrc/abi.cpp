@@ -196,17 +196,45 @@ bsq_status bsq_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_scale
     const int grid = persistent_grid();
     if (dg && m_total > 0) {
         bsq::BwdArgs a{dy_codes, dy_scale, wt_codes, wt_scale, nullptr, nullptr, nullptr, nullptr,
-                       offsets, num_experts, m_total, n, k, P, Pw, dx, dx_dtype == BSQ_F32 ? 1 : 0, 0, plan0};
+                       offsets, num_experts, m_total, n, k, P, Pw, dx, dx_dtype == BSQ_F32 ? 1 : 0, 0, plan0, 0};
         const hipError_t e = bsq::launch_gemm_bwd_mxfp8(a, grid, stream);
         if (e != hipSuccess) return BSQ_ERR_HIP;
     }
     if (wg) {
         bsq::BwdArgs a{nullptr, nullptr, nullptr, nullptr, dyt_codes, dyt_scale, xt_codes, xt_scale,
-                       offsets, num_experts, m_total, n, k, P, Pw, dw, dw_dtype == BSQ_F32 ? 1 : 0, 1, plan1};
+                       offsets, num_experts, m_total, n, k, P, Pw, dw, dw_dtype == BSQ_F32 ? 1 : 0, 1, plan1, 0};
         const hipError_t e = bsq::launch_gemm_bwd_mxfp8(a, grid, stream);
         if (e != hipSuccess) return BSQ_ERR_HIP;
     }
     return BSQ_OK;
+}
+
+bsq_status bsq_grouped_gemm_fwd_mxfp8(const uint8_t* x_codes, const uint8_t* x_scale, const uint8_t* w_codes,
+                                      const uint8_t* w_scale, const int32_t* offsets, int32_t num_experts,
+                                      int64_t m_total, int64_t n, int64_t k, void* y, bsq_dtype y_dtype,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_experts < 1 || m_total < 0 || n < 0 || k < 0) return BSQ_ERR_INVALID_ARG;
+    if (y_dtype != BSQ_BF16 && y_dtype != BSQ_F32) return BSQ_ERR_INVALID_ARG;
+    if (!offsets || !workspace || !w_codes || !w_scale) return BSQ_ERR_INVALID_ARG;
+    if (m_total > 0 && (!x_codes || !x_scale || !y)) return BSQ_ERR_INVALID_ARG;
+    if (num_experts > bsq::MAX_EXPERTS) return BSQ_ERR_UNSUPPORTED;
+    if (n == 0 || k == 0 || n % 64 || k % 64) return BSQ_ERR_UNSUPPORTED;
+    if (!aligned(workspace, 256) || !aligned(w_codes, 16) || (m_total > 0 && !aligned(x_codes, 16)))
+        return BSQ_ERR_UNSUPPORTED;
+    // 32-bit per-tile offsets: 256 rows of codes; block-major scale runs
+    const int64_t wrows = (int64_t)num_experts * n;
+    if (256 * k >= kMaxBufferOffset || m_total >= (int64_t)1 << 31 ||
+        (k / 32 + 1) * (m_total + 256) >= kMaxBufferOffset || (k / 32 + 1) * (wrows + 256) >= kMaxBufferOffset)
+        return BSQ_ERR_UNSUPPORTED;
+    if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, n, k))
+        return BSQ_ERR_WORKSPACE_TOO_SMALL;
+    if (m_total == 0) return BSQ_OK;
+    // the dgrad tile path with a row-major weight stack as B: reduction k,
+    // output width n
+    bsq::BwdArgs a{x_codes, x_scale, w_codes, w_scale, nullptr, nullptr, nullptr, nullptr,
+                   offsets, num_experts, m_total, k, n, 0, 0, y, y_dtype == BSQ_F32 ? 1 : 0, 0,
+                   static_cast<int32_t*>(workspace), 1};
+    return bsq::launch_gemm_bwd_mxfp8(a, persistent_grid(), stream) == hipSuccess ? BSQ_OK : BSQ_ERR_HIP;
 }
 
 bsq_status bsq_debug_status(const void* workspace, hipStream_t stream, int32_t* error_word_host) {

@@ -150,8 +150,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             // block-major scales: block j of rows r0.. starts at base + j * rows_total + r0
             a = p.dy_codes + m0 * p.N; as = p.dy_scale + m0;
             lda = p.N; ldas = p.m_total; rows_a = (int)min((int64_t)BWD_BM, off1 - m0);
-            b = p.wt_codes + k0 * p.Pw + cw; bs = p.wt_scale + (cw / 32) * p.K + k0;
-            ldb = p.Pw; ldbs = p.K; rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
+            if (p.b_rows) {
+                // forward MXFP8: rows k0.. of expert e's [K][N] weight block
+                b = p.wt_codes + ((int64_t)e * p.K + k0) * p.N; bs = p.wt_scale + (int64_t)e * p.K + k0;
+                ldb = p.N; ldbs = (int64_t)p.E * p.K;
+            } else {
+                b = p.wt_codes + k0 * p.Pw + cw; bs = p.wt_scale + (cw / 32) * p.K + k0;
+                ldb = p.Pw; ldbs = p.K;
+            }
+            rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
             R = p.N;
             c = reinterpret_cast<char*>(p.out) + (m0 * p.K + k0) * esz; ldc = p.K;
         } else {

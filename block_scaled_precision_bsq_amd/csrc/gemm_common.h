@@ -151,6 +151,11 @@ struct BwdArgs {
     void* out; int out_f32;
     int wgrad;   // 0: dgrad tiles, 1: wgrad tiles
     int32_t* plan;
+    // dgrad tiles only: 0 = B is the COLWISE_T weight transpose Wt [K][Pw]
+    // (expert e at column e*(N+32)); 1 = B is a ROWWISE MXFP8 weight stack
+    // W [E*K][N] with block-major scales [N/32][E*K] (the forward MXFP8 GEMM,
+    // whose reduction is N here and whose output width is K).
+    int b_rows;
 };
 
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t m_total, int mode, int bm, int nt, int kt,

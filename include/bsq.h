@@ -209,6 +209,32 @@ bsq_status bsq_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_scale
                                 int64_t k, void* dx, bsq_dtype dx_dtype, void* dw, bsq_dtype dw_dtype,
                                 unsigned flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * bsq_grouped_gemm_fwd_mxfp8 -- forward expert grouped GEMM over MXFP8
+ * operands: y[m][j] = sum_k x[m][k] * W_e[j][k] for every row m of expert e's
+ * segment, with x and W quantized to MXFP8 along k.  This is the all-MXFP8
+ * expert GEMM ("Composer 2 Technical Report", section 3.1: continued
+ * pretraining runs in MXFP8; "Scaling and Optimizing Frontier Model
+ * Training", MXFP8 expert kernels: MXFP8 grouped GEMMs in forward and
+ * backward), next to the NVFP4-variant forward of bsq_grouped_gemm_fwd.
+ *   x_codes/x_scale: MXFP8 ROWWISE of x [m_total][k] (scale [k/32][m_total]).
+ *   w_codes/w_scale: MXFP8 ROWWISE of W viewed as [num_experts*n][k] (rows
+ *   e*n + j; scale [k/32][num_experts*n]).
+ *   y [m_total][n] in y_dtype (bf16 round-to-nearest-even, or f32).
+ * Products are formed by the block-scaled MFMA and accumulated in fp32 in a
+ * fixed order per element (the same kernel and tolerance as BSQ_DGRAD).
+ *   n % 64 == 0, k % 64 == 0, num_experts >= 1.
+ *   workspace >= bsq_workspace_size(BSQ_OP_GEMM_FWD, ...) bytes, 256-byte
+ *   aligned; its contents are scratch.
+ * Errors: INVALID_ARG, UNSUPPORTED (multiples, alignment, sizes beyond the
+ *   kernel's 32-bit offsets), WORKSPACE_TOO_SMALL, HIP.
+ */
+bsq_status bsq_grouped_gemm_fwd_mxfp8(const uint8_t* x_codes, const uint8_t* x_scale,
+                                      const uint8_t* w_codes, const uint8_t* w_scale,
+                                      const int32_t* offsets, int32_t num_experts, int64_t m_total, int64_t n,
+                                      int64_t k, void* y, bsq_dtype y_dtype, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace the GEMM entry points need (host function, no GPU use).
  * op is BSQ_OP_GEMM_FWD or BSQ_OP_GEMM_BWD; returns 0 for invalid arguments. */
 size_t bsq_workspace_size(int op, int32_t num_experts, int64_t m_total, int64_t n, int64_t k);

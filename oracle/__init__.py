@@ -239,6 +239,35 @@ def grouped_gemm_fwd(a_q, w_q, offsets, rows=None) -> np.ndarray:
     return y
 
 
+def grouped_gemm_fwd_mxfp8(x_q, w_q, offsets, rows=None, absolute=False) -> np.ndarray:
+    """All-MXFP8 forward expert GEMM ("Composer 2 Technical Report" section
+    3.1, continued pretraining in MXFP8; "Scaling and Optimizing Frontier
+    Model Training", MXFP8 expert kernels), in float64:
+    Y[m, j] = sum_k X_hat[m, k] * W_hat_e[j, k] for m in segment e.
+
+    ``x_q`` = ROWWISE MXFP8 of X [M, K]; ``w_q`` = ROWWISE MXFP8 of the
+    weights stacked as [E*N, K] (expert e owns rows e*N .. e*N+N-1); scales
+    block-major.  ``absolute=True``: sums of absolute products instead.
+    """
+    off = np.asarray(offsets, np.int64)
+    E = len(off) - 1
+    M = x_q[0].shape[0]
+    N = w_q[0].shape[0] // E
+    rows = np.arange(M) if rows is None else np.asarray(rows, np.int64)
+    exp_of = _expert_of_rows(off, rows)
+    y = np.zeros((len(rows), N), np.float64)
+    for e in np.unique(exp_of):
+        sel = np.nonzero(exp_of == e)[0]
+        r = rows[sel]
+        x_hat = dequant_mxfp8(x_q[0][r], x_q[1][:, r])
+        sl = slice(int(e) * N, (int(e) + 1) * N)
+        w_hat = dequant_mxfp8(w_q[0][sl], w_q[1][:, sl])
+        if absolute:
+            x_hat, w_hat = np.abs(x_hat), np.abs(w_hat)
+        y[sel] = x_hat @ w_hat.T
+    return y
+
+
 def grouped_gemm_dgrad(dy_q, wt_q, offsets, n, rows=None, absolute=False) -> np.ndarray:
     """dX[m, k] = sum_n dY_hat[m, n] * W_hat_e[n, k] (float64).
 

@@ -190,6 +190,36 @@ def test_wgrad_matches_exact_blocks_and_outer_products(orc):
         assert not dyh[:, m1 - m0:].any() and not xh[:, m1 - m0:].any()
 
 
+def test_fwd_mxfp8_matches_exact_blocks(orc):
+    """All-MXFP8 forward: per-expert products equal the exact int64 block sums
+    (ROWWISE codes of X rows against ROWWISE codes of the expert's weight
+    rows); rows of empty experts do not exist and every row is attributed to
+    the expert its offsets give."""
+    rng = np.random.default_rng(28)
+    counts = [9, 0, 40, 1]
+    E, n, k = len(counts), 64, 96
+    off = offsets_from_counts(counts)
+    M = int(off[-1])
+    x = make_quantize_input(rng, M, k)
+    w = normal_bf16(rng, (E * n, k), 0.02)
+    x_q, w_q = orc.quantize_mxfp8_rowwise(x), orc.quantize_mxfp8_rowwise(w)
+    y = orc.grouped_gemm_fwd_mxfp8(x_q, w_q, off)
+    ya = orc.grouped_gemm_fwd_mxfp8(x_q, w_q, off, absolute=True)
+    for e in range(E):
+        m0, m1 = int(off[e]), int(off[e + 1])
+        if m0 == m1:
+            continue
+        ref, absum = _mx_exact_tn(x_q[0][m0:m1], x_q[1][:, m0:m1], w_q[0][e * n:(e + 1) * n],
+                                  w_q[1][:, e * n:(e + 1) * n])
+        assert np.all(np.abs(y[m0:m1] - ref) <= 1e-12 * absum + 1e-300)
+        # absolute sums: the same exact block sums over magnitudes (sign bit 7 cleared)
+        ref_abs, _ = _mx_exact_tn(x_q[0][m0:m1] & 0x7F, x_q[1][:, m0:m1], w_q[0][e * n:(e + 1) * n] & 0x7F,
+                                  w_q[1][:, e * n:(e + 1) * n])
+        assert np.allclose(ya[m0:m1], ref_abs, rtol=1e-12, atol=0)
+    rows = np.array([M - 1, 0, 20])
+    assert np.array_equal(orc.grouped_gemm_fwd_mxfp8(x_q, w_q, off, rows=rows), y[rows])
+
+
 def test_single_expert_is_dense(orc):
     """With offsets [0, M] the grouped fwd equals one dense product of the
     dequantized matrices, and dequantized values are the bf16 inputs to
