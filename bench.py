@@ -285,6 +285,24 @@ def quantize_config2(bsq, torch, dev, reps=20):
         us = a.elapsed_time(b) * 1e3 / reps
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 2), "bytes": nbytes, "gbps": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_GBS, 4)}
+    # Ablation (not the method): the same quantizer with fast approximate
+    # divides; how many decisions it changes against IEEE division, and its time.
+    bsq.bsq_quantize_nvfp4v(x, *nv)
+    fc, fb, fr = bsq.bsq_debug_quantize_nvfp4v_fastdiv(x)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        bsq.bsq_debug_quantize_nvfp4v_fastdiv(x)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    nib = lambda c: torch.stack([c & 15, c >> 4], -1)
+    out["nvfp4v_fastdiv_ablation"] = {
+        "us": round(us, 2), "speedup_vs_ieee": round(out["nvfp4v"]["us"] / us, 3),
+        "codes_changed_frac": float((nib(fc) != nib(nv[0])).double().mean()),
+        "bscale_changed_frac": float((fb != nv[1]).double().mean()),
+        "rscale_changed_frac": float((fr != nv[2]).double().mean()),
+    }
     return out
 
 

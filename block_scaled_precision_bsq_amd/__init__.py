@@ -36,6 +36,7 @@ BSQ_OP_GEMM_FWD, BSQ_OP_GEMM_BWD = 0, 1
 _SIGS = {
     "bsq_quantize_nvfp4v": ([P, I64, I64, I64, P, I32, P, P, P, P], INT),
     "bsq_swiglu_quantize_nvfp4v": ([P, I64, I64, I64, P, I64, P, P, P, P], INT),
+    "bsq_debug_quantize_nvfp4v_fastdiv": ([P, I64, I64, I64, P, P, P, P], INT),
     "bsq_quantize_mxfp8": ([P, I64, I64, I64, INT, P, I32, P, P, P], INT),
     "bsq_grouped_gemm_fwd": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_bwd": ([P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, INT, ctypes.c_uint, P,
@@ -124,6 +125,21 @@ def bsq_quantize_nvfp4v(x, codes=None, bscale=None, rscale=None, offsets=None, s
     _check("bsq_quantize_nvfp4v",
            _lib.bsq_quantize_nvfp4v(_ptr(x), rows, cols, ld, _ptr(offsets), ng, _ptr(codes), _ptr(bscale),
                                     _ptr(rscale), _stream(stream)))
+    return codes, bscale, rscale
+
+
+def bsq_debug_quantize_nvfp4v_fastdiv(x, stream=None):
+    """Ablation: bsq_quantize_nvfp4v with fast approximate divides (reciprocal
+    approximation times numerator).  Returns (codes, bscale, rscale)."""
+    _dev(x, "x", _BF16)
+    rows, cols, ld = _rows_ld(x)
+    dev = x.device
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    bscale = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    rscale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    _check("bsq_debug_quantize_nvfp4v_fastdiv",
+           _lib.bsq_debug_quantize_nvfp4v_fastdiv(_ptr(x), rows, cols, ld, _ptr(codes), _ptr(bscale), _ptr(rscale),
+                                                  _stream(stream)))
     return codes, bscale, rscale
 
 

@@ -14,6 +14,8 @@ namespace bsq {
 hipError_t launch_quantize_nvfp4v(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, float*, hipStream_t);
 hipError_t launch_swiglu_quantize_nvfp4v(const uint16_t*, int64_t, int, int64_t, uint16_t*, int64_t, uint8_t*, uint8_t*,
                                          float*, hipStream_t);
+hipError_t launch_quantize_nvfp4v_fastdiv(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, float*,
+                                          hipStream_t);
 hipError_t launch_quantize_mxfp8_rowwise(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, hipStream_t);
 hipError_t launch_quantize_mxfp8_colwise_t(const uint16_t*, int64_t, int, int64_t, const int32_t*, int, int64_t,
                                            uint8_t*, uint8_t*, hipStream_t);
@@ -89,6 +91,18 @@ bsq_status bsq_quantize_nvfp4v(const void* x_bf16, int64_t rows, int64_t cols, i
     if (rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
     return from_hip(bsq::launch_quantize_nvfp4v(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x, codes,
                                                 bscale, rscale, stream));
+}
+
+bsq_status bsq_debug_quantize_nvfp4v_fastdiv(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                             uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t stream) {
+    if (rows < 0 || cols < 0) return BSQ_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return BSQ_OK;
+    if (!x_bf16 || !codes || !bscale || !rscale || ld_x < cols) return BSQ_ERR_INVALID_ARG;
+    if (cols % 16 || cols > 16384 || ld_x % 8 || !aligned(x_bf16, 16) || !aligned(codes, 8) || !aligned(rscale, 4))
+        return BSQ_ERR_UNSUPPORTED;
+    if (rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
+    return from_hip(bsq::launch_quantize_nvfp4v_fastdiv(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x,
+                                                        codes, bscale, rscale, stream));
 }
 
 bsq_status bsq_swiglu_quantize_nvfp4v(const void* gu_bf16, int64_t rows, int64_t inter, int64_t ld_gu, void* h_bf16,

@@ -51,7 +51,17 @@ __device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
     return pack_bf16x2(silu_mul(bf16_lo(gw), bf16_lo(uw)), silu_mul(bf16_hi(gw), bf16_hi(uw)));
 }
 
-template <int BPL, bool SWIGLU>
+// FASTDIV (ablation only, not the method): every division of the row
+// quantizer -- A / 2688, 448 a_b / A and x / d_b -- is replaced by the
+// hardware reciprocal approximation times the numerator (v_rcp_f32, then
+// v_mul_f32), the kind of fast divide the report warns against for NVFP4.
+// Used to count the codes such a divide changes.
+__device__ __forceinline__ float rcp_approx(float b) {
+    asm volatile("" : "+v"(b));  // keep the reciprocal a run-time instruction
+    return __builtin_amdgcn_rcpf(b);
+}
+
+template <int BPL, bool SWIGLU, bool FASTDIV = false>
 __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restrict__ x, int64_t rows,
                                                          int cols, int64_t ldx, uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ bscale,
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restr
         return;
     }
     const float A = __uint_as_float(rmax << 16);
-    const float s_row = A / 2688.0f;  // IEEE binary32 division
+    const float s_row = FASTDIV ? A * rcp_approx(2688.0f) : A / 2688.0f;  // IEEE binary32 division
     if (lane == 0) rscale[row] = s_row;
 
 #pragma unroll
@@ -128,20 +138,29 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restr
         float num, den;
         if (ab <= 0x1p119f) { num = 448.0f * ab; den = A; }
         else                { num = 1.75f * ab;  den = A * 0x1p-8f; }
-        const float t = num / den;  // in [0, 448]
+        const float t = FASTDIV ? num * rcp_approx(den) : num / den;  // in [0, 448]
         const uint32_t S = e4m3x4(t, 0.0f, 0.0f, 0.0f) & 0xFFu;
         br[b] = (uint8_t)S;
         const float d = e4m3_value(S) * s_row;
         uint2 out = make_uint2(0, 0);
         if (d != 0.0f) {
-            const double inv = 1.0 / (double)d;
             float q[16];
             const uint32_t w[8] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w,
                                    v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
+            if constexpr (FASTDIV) {
+                const float r = rcp_approx(d);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                q[2 * j] = (float)((double)bf16_lo(w[j]) * inv);
-                q[2 * j + 1] = (float)((double)bf16_hi(w[j]) * inv);
+                for (int j = 0; j < 8; ++j) {
+                    q[2 * j] = bf16_lo(w[j]) * r;
+                    q[2 * j + 1] = bf16_hi(w[j]) * r;
+                }
+            } else {
+                const double inv = 1.0 / (double)d;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    q[2 * j] = (float)((double)bf16_lo(w[j]) * inv);
+                    q[2 * j + 1] = (float)((double)bf16_hi(w[j]) * inv);
+                }
             }
             uint32_t c0 = e2m1x2<0>(0u, q[0], q[1]);
             c0 = e2m1x2<1>(c0, q[2], q[3]);
@@ -412,14 +431,14 @@ __global__ void k_debug_e4m3(const float* __restrict__ in, uint8_t* __restrict__
 
 // ---------------------------------------------------------------- launchers
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool FASTDIV = false>
 static hipError_t launch_nvfp4v(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
                                 uint8_t* bscale, float* rscale, uint16_t* h, int64_t ldh, hipStream_t s) {
     const int nb = cols / 16;
     const dim3 grid((unsigned)((rows + 3) / 4));
-#define BSQ_NVFP4V_LAUNCH(BPL)                                                                                \
-    hipLaunchKernelGGL((k_quantize_nvfp4v<BPL, SWIGLU>), grid, dim3(256), 0, s, x, rows, cols, ldx, codes, \
-                       bscale, rscale, h, ldh)
+#define BSQ_NVFP4V_LAUNCH(BPL)                                                                       \
+    hipLaunchKernelGGL((k_quantize_nvfp4v<BPL, SWIGLU, FASTDIV>), grid, dim3(256), 0, s, x, rows, cols, \
+                       ldx, codes, bscale, rscale, h, ldh)
     if (nb <= 64)
         BSQ_NVFP4V_LAUNCH(1);
     else if (nb <= 128)
@@ -439,6 +458,11 @@ static hipError_t launch_nvfp4v(const uint16_t* x, int64_t rows, int cols, int64
 hipError_t launch_quantize_nvfp4v(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
                                   uint8_t* bscale, float* rscale, hipStream_t s) {
     return launch_nvfp4v<false>(x, rows, cols, ldx, codes, bscale, rscale, nullptr, 0, s);
+}
+
+hipError_t launch_quantize_nvfp4v_fastdiv(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
+                                          uint8_t* bscale, float* rscale, hipStream_t s) {
+    return launch_nvfp4v<false, true>(x, rows, cols, ldx, codes, bscale, rscale, nullptr, 0, s);
 }
 
 hipError_t launch_swiglu_quantize_nvfp4v(const uint16_t* gu, int64_t rows, int inter, int64_t ldgu, uint16_t* h,

@@ -137,6 +137,20 @@ bsq_status bsq_swiglu_quantize_nvfp4v(const void* gu_bf16, int64_t rows, int64_t
                                       uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t stream);
 
 /*
+ * bsq_debug_quantize_nvfp4v_fastdiv -- ABLATION, not the method: the NVFP4
+ * variant quantizer of bsq_quantize_nvfp4v with every division (A/2688,
+ * 448*a_b/A and x/d_b) replaced by a fast approximate divide, numerator times
+ * the hardware reciprocal approximation (v_rcp_f32).  "Composer 2 Technical
+ * Report", section 6.1, reports that such a fast divide in NVFP4 quantization
+ * made RL training diverge after about a hundred steps and that IEEE
+ * division is required; this entry point exists to count how many codes,
+ * block scales and row scales the approximation changes.  Same arguments,
+ * layouts and errors as bsq_quantize_nvfp4v (no offsets).
+ */
+bsq_status bsq_debug_quantize_nvfp4v_fastdiv(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                             uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t stream);
+
+/*
  * bsq_quantize_mxfp8 -- MXFP8 quantization ("Composer 2 Technical Report",
  * section 6.1, MXFP8 in the MoE backward: E4M3 values, E8M0 scale per 32).
  * Per block of 32: A = max|x|; A == 0 gives scale byte 0 and codes 0; else

@@ -168,6 +168,33 @@ def quantize_mxfp8_rowwise(x_bf16: np.ndarray):
     return codes, scale
 
 
+def nvfp4v_decision_margins(x_bf16: np.ndarray, delta: float):
+    """Which decisions of the NVFP4-variant quantizer a divide with relative
+    error up to ``delta`` could change ("Composer 2 Technical Report", section
+    6.1: the quantizer needs IEEE division; a fast approximate divide made
+    training diverge).  With exact division, block b's scale byte is
+    E4M3(448 a_b / A) and element x's code is E2M1(x / d_b); a perturbed
+    divide can change a decision only if the exact argument lies within
+    ``delta`` (relative) of a rounding boundary of its encoder, i.e. if the
+    encoder maps arg * (1 - delta) and arg * (1 + delta) to different codes.
+    Returns (blocks_at_risk [rows, cols/16], elements_at_risk [rows, cols]),
+    the elements judged against the exact-division d_b."""
+    x = _bf16(x_bf16)
+    rows, cols = x.shape
+    codes, bscale, rscale = quantize_nvfp4v(x)
+    xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    a_b = np.abs(xf).reshape(rows, cols // 16, 16).max(-1)
+    A = a_b.max(-1, keepdims=True) if cols else np.zeros((rows, 1))
+    t = np.divide(448.0 * a_b, A, out=np.zeros_like(a_b), where=A > 0)
+    blocks = e4m3_encode(t * (1 - delta)) != e4m3_encode(t * (1 + delta))
+    _, e4m3_tab, _ = tables()
+    d = (e4m3_tab[bscale].astype(np.float32) * rscale[:, None].astype(np.float32)).astype(np.float64)  # RN32
+    d = np.repeat(d, 16, axis=1)
+    q = np.divide(xf, d, out=np.zeros_like(xf), where=d > 0)
+    elems = e2m1_encode(q * (1 - delta)) != e2m1_encode(q * (1 + delta))
+    return blocks, elems
+
+
 def padded_cols(ngroups: int, rows: int) -> int:
     return int(lib().orc_colwise_padded_cols(ngroups, rows))
 

@@ -252,3 +252,29 @@ def test_mxfp8_colwise_t_matches_rowwise_on_transposed_segments(orc):
     assert not codes[:, ~covered].any()
     assert not scale[~covered[::32], :].any()
     assert covered.sum() <= P
+
+
+def test_decision_margins_flag_exactly_the_boundaries(orc):
+    """Elements placed exactly on E2M1 rounding midpoints (ties) are at risk
+    for any delta > 0; elements on E2M1 grid values are not (their nearest
+    boundary is at least 1/12 away relative); block scales on an exact E4M3
+    tie are at risk."""
+    from conftest import bf16
+    # one row with A = 2688, so s_row = 1.  Block 0: t = 448, d = 448, its
+    # elements sit at 6 and far below 0.25 (no boundary near).  Block 1: amax
+    # 6 gives t = 1, d = 1: elements on the ties 2.5, -0.75, 1.25 and on the
+    # grid value 6.  Block 2: t = 448 * 1088 / 2688 = 181.33 (E4M3 neighbours
+    # 176 and 192, midpoint 184: no tie).  Block 3: t = 448 * 102 / 2688 = 17,
+    # the E4M3 tie between 16 and 18.
+    row = np.zeros(64)
+    row[:8] = [2688, 6, 4, 3, 2, 1.5, 1, 0.5]
+    row[16:20] = [2.5, -0.75, 1.25, 6]
+    row[32] = 1088
+    row[48] = 102
+    blocks, elems = orc.nvfp4v_decision_margins(bf16(row)[None, :], 2.0 ** -20)
+    assert not elems[0, :8].any()
+    assert elems[0, 16] and elems[0, 17] and elems[0, 18] and not elems[0, 19]
+    assert not blocks[0, 0] and not blocks[0, 2] and blocks[0, 3]
+    # a value far from every boundary stays safe for a large delta as well
+    _, e2 = orc.nvfp4v_decision_margins(bf16(row)[None, :], 2.0 ** -6)
+    assert not e2[0, :8].any()
