@@ -224,6 +224,7 @@ def main():
     quant = quantize_config2(bsq, torch, dev)
     fwd_mx = fwd_mxfp8_compare(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M,
                                {k: stage_ms[k] for k in ("gemm_fwd_gate_up", "gemm_fwd_down")}, ws_f)
+    bf16_base = bf16_baseline(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, stage_ms, fwd_mx, ws_f)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -244,6 +245,7 @@ def main():
         "breakdown": breakdown,
         "quantize": quant,
         "fwd_mxfp8": fwd_mx,
+        "bf16_baseline": bf16_base,
     }
     print(json.dumps(out))
 
@@ -338,6 +340,38 @@ def fwd_mxfp8_compare(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, nv_ms
         out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK["fp8"], 4),
                      "speedup_vs_nvfp4v_fwd": round(nv_ms[name] / ms, 3)}
     del q, y_gu, y_dn
+    return out
+
+
+def bf16_baseline(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, stage_ms, fwd_mx, ws, reps=10):
+    """The forward expert GEMMs on plain bf16 operands with the same tiles,
+    pipeline and scheduler (bsq_grouped_gemm_bf16), outside the step: the
+    baseline the block-scaled GEMMs are compared with."""
+    y_gu = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    y_dn = torch.empty((M, Hd), dtype=torch.bfloat16, device=dev)
+    cases = {
+        "gemm_fwd_gate_up": (lambda: bsq.bsq_grouped_gemm_bf16(x, w_gu, off, 2 * I, Hd, y=y_gu, workspace=ws),
+                             2.0 * M * 2 * I * Hd),
+        "gemm_fwd_down": (lambda: bsq.bsq_grouped_gemm_bf16(h, w_dn, off, Hd, I, y=y_dn, workspace=ws),
+                          2.0 * M * Hd * I),
+    }
+    stream = torch.cuda.current_stream()
+    out = {"operands": "bf16 activations and weights, bf16 MFMA, bf16 out"}
+    for name, (fn, fl) in cases.items():
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK["f16"], 4),
+                     "speedup_nvfp4v_fwd_vs_bf16": round(ms / stage_ms[name], 3),
+                     "speedup_mxfp8_fwd_vs_bf16": round(ms / fwd_mx[name]["ms"], 3)}
+    del y_gu, y_dn
     return out
 
 

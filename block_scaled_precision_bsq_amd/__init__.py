@@ -42,6 +42,7 @@ _SIGS = {
     "bsq_grouped_gemm_bwd": ([P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, INT, ctypes.c_uint, P,
                               ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_fwd_mxfp8": ([P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
+    "bsq_grouped_gemm_bf16": ([P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
     "bsq_workspace_size": ([INT, I32, I64, I64, I64], ctypes.c_size_t),
     "bsq_colwise_padded_cols": ([I32, I64], I64),
     "bsq_status_string": ([INT], ctypes.c_char_p),
@@ -252,6 +253,27 @@ def bsq_grouped_gemm_fwd_mxfp8(x_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None
            _lib.bsq_grouped_gemm_fwd_mxfp8(_ptr(x_codes), _ptr(x_scale), _ptr(w_codes), _ptr(w_scale),
                                            _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype, _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    return y
+
+
+def bsq_grouped_gemm_bf16(x, w, offsets, n, k, y_dtype=BSQ_BF16, y=None, workspace=None, stream=None):
+    """bf16 baseline grouped GEMM: x [m_total, k] bf16, w [E*n, k] bf16."""
+    _dev(x, "x", _BF16)
+    _dev(w, "w", _BF16)
+    _dev(offsets, "offsets", (torch.int32,))
+    E = offsets.numel() - 1
+    m_total = x.shape[0]
+    for t, nm, shape in ((x, "x", (m_total, k)), (w, "w", (E * n, k))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous with shape {shape}")
+    dev = x.device
+    if y is None:
+        y = torch.empty((m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev)
+    _check("bsq_grouped_gemm_bf16",
+           _lib.bsq_grouped_gemm_bf16(_ptr(x), _ptr(w), _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype,
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
     return y
 
 

@@ -210,13 +210,13 @@ bsq_status bsq_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_scale
     const int grid = persistent_grid();
     if (dg && m_total > 0) {
         bsq::BwdArgs a{dy_codes, dy_scale, wt_codes, wt_scale, nullptr, nullptr, nullptr, nullptr,
-                       offsets, num_experts, m_total, n, k, P, Pw, dx, dx_dtype == BSQ_F32 ? 1 : 0, 0, plan0, 0};
+                       offsets, num_experts, m_total, n, k, P, Pw, dx, dx_dtype == BSQ_F32 ? 1 : 0, 0, plan0, 0, 0};
         const hipError_t e = bsq::launch_gemm_bwd_mxfp8(a, grid, stream);
         if (e != hipSuccess) return BSQ_ERR_HIP;
     }
     if (wg) {
         bsq::BwdArgs a{nullptr, nullptr, nullptr, nullptr, dyt_codes, dyt_scale, xt_codes, xt_scale,
-                       offsets, num_experts, m_total, n, k, P, Pw, dw, dw_dtype == BSQ_F32 ? 1 : 0, 1, plan1, 0};
+                       offsets, num_experts, m_total, n, k, P, Pw, dw, dw_dtype == BSQ_F32 ? 1 : 0, 1, plan1, 0, 0};
         const hipError_t e = bsq::launch_gemm_bwd_mxfp8(a, grid, stream);
         if (e != hipSuccess) return BSQ_ERR_HIP;
     }
@@ -247,7 +247,28 @@ bsq_status bsq_grouped_gemm_fwd_mxfp8(const uint8_t* x_codes, const uint8_t* x_s
     // output width n
     bsq::BwdArgs a{x_codes, x_scale, w_codes, w_scale, nullptr, nullptr, nullptr, nullptr,
                    offsets, num_experts, m_total, k, n, 0, 0, y, y_dtype == BSQ_F32 ? 1 : 0, 0,
-                   static_cast<int32_t*>(workspace), 1};
+                   static_cast<int32_t*>(workspace), 1, 0};
+    return bsq::launch_gemm_bwd_mxfp8(a, persistent_grid(), stream) == hipSuccess ? BSQ_OK : BSQ_ERR_HIP;
+}
+
+bsq_status bsq_grouped_gemm_bf16(const void* x_bf16, const void* w_bf16, const int32_t* offsets,
+                                 int32_t num_experts, int64_t m_total, int64_t n, int64_t k, void* y,
+                                 bsq_dtype y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_experts < 1 || m_total < 0 || n < 0 || k < 0) return BSQ_ERR_INVALID_ARG;
+    if (y_dtype != BSQ_BF16 && y_dtype != BSQ_F32) return BSQ_ERR_INVALID_ARG;
+    if (!offsets || !workspace || !w_bf16) return BSQ_ERR_INVALID_ARG;
+    if (m_total > 0 && (!x_bf16 || !y)) return BSQ_ERR_INVALID_ARG;
+    if (num_experts > bsq::MAX_EXPERTS) return BSQ_ERR_UNSUPPORTED;
+    if (n == 0 || k == 0 || n % 64 || k % 64) return BSQ_ERR_UNSUPPORTED;
+    if (!aligned(workspace, 256) || !aligned(w_bf16, 16) || (m_total > 0 && !aligned(x_bf16, 16)))
+        return BSQ_ERR_UNSUPPORTED;
+    if (256 * 2 * k >= kMaxBufferOffset || m_total >= (int64_t)1 << 31) return BSQ_ERR_UNSUPPORTED;
+    if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, n, k))
+        return BSQ_ERR_WORKSPACE_TOO_SMALL;
+    if (m_total == 0) return BSQ_OK;
+    bsq::BwdArgs a{static_cast<const uint8_t*>(x_bf16), nullptr, static_cast<const uint8_t*>(w_bf16), nullptr,
+                   nullptr, nullptr, nullptr, nullptr, offsets, num_experts, m_total, k, n, 0, 0, y,
+                   y_dtype == BSQ_F32 ? 1 : 0, 0, static_cast<int32_t*>(workspace), 1, 1};
     return bsq::launch_gemm_bwd_mxfp8(a, persistent_grid(), stream) == hipSuccess ? BSQ_OK : BSQ_ERR_HIP;
 }
 

@@ -87,13 +87,39 @@ struct BwdTile {
     uint32_t vsa[4];  // dgrad A scale rows (one byte per lane)
 };
 
-template <bool OUT_F32, bool WGRAD>
+// One 64-byte k step of fragments for output block (i, j): a single
+// block-scaled fp8 MFMA (64 k), or for bf16 operands two bf16 MFMAs (16 k
+// each) on the same 32 bytes per lane -- bytes [16g, +16) then [32+16g, +16),
+// i.e. elements 8g.. and 16+8g.. of the 32 the step holds, the bf16 MFMA's
+// k order for lane group g.
+template <bool BF16>
+__device__ __forceinline__ float16v mfma_step(const int8v& a, const int8v& b, int sa, int sb, float16v c) {
+    if constexpr (BF16) {
+        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+        typedef int int4v __attribute__((ext_vector_type(4)));
+        const int4v alo = {a[0], a[1], a[2], a[3]}, ahi = {a[4], a[5], a[6], a[7]};
+        const int4v blo = {b[0], b[1], b[2], b[3]}, bhi = {b[4], b[5], b[6], b[7]};
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, alo), __builtin_bit_cast(bf16x8, blo),
+                                                    c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ahi),
+                                                       __builtin_bit_cast(bf16x8, bhi), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+    }
+}
+
+// BF16: the same tile loop over plain bf16 operands (the bf16 baseline of
+// the expert GEMM): no scales, a k step is 32 elements (64 bytes) and the
+// reduction length is counted in bytes.
+template <bool OUT_F32, bool WGRAD, bool BF16>
 __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     // DMA instructions per wave per super-stage: 16 code rows, the A scales
     // (four 64-byte pieces of block-major bytes for dgrad, whose token rows
     // start anywhere; one packed 256-byte block for wgrad, whose rows start
-    // at a multiple of 256) and one packed 256-byte block of B scales.
-    constexpr int SS_DMA = WGRAD ? 18 : 21;
+    // at a multiple of 256) and one packed 256-byte block of B scales; bf16
+    // operands carry no scales.
+    static_assert(!(BF16 && WGRAD), "the bf16 mode runs the row-ragged tiles only");
+    constexpr int SS_DMA = BF16 ? 16 : (WGRAD ? 18 : 21);
     extern __shared__ __align__(16) uint8_t smem_raw[];
     __shared__ int s_tile;
 
@@ -150,7 +176,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             // block-major scales: block j of rows r0.. starts at base + j * rows_total + r0
             a = p.dy_codes + m0 * p.N; as = p.dy_scale + m0;
             lda = p.N; ldas = p.m_total; rows_a = (int)min((int64_t)BWD_BM, off1 - m0);
-            if (p.b_rows) {
+            if constexpr (BF16) {
+                // bf16 rows: x [M][N] and expert e's weight rows [K][N], 2 bytes each
+                a = p.dy_codes + m0 * p.N * 2; as = p.dy_codes;
+                lda = 2 * p.N; ldas = 0;
+                b = p.wt_codes + ((int64_t)e * p.K + k0) * p.N * 2; bs = p.wt_codes;
+                ldb = 2 * p.N; ldbs = 0;
+            } else if (p.b_rows) {
                 // forward MXFP8: rows k0.. of expert e's [K][N] weight block
                 b = p.wt_codes + ((int64_t)e * p.K + k0) * p.N; bs = p.wt_scale + (int64_t)e * p.K + k0;
                 ldb = p.N; ldbs = (int64_t)p.E * p.K;
@@ -159,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                 ldb = p.Pw; ldbs = p.K;
             }
             rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
-            R = p.N;
+            R = BF16 ? 2 * p.N : p.N;  // bytes of k per row
             c = reinterpret_cast<char*>(p.out) + (m0 * p.K + k0) * esz; ldc = p.K;
         } else {
             // dW_e[n][k] = sum_{m in e} dY^T[n][m] X^T[k][m]
@@ -212,6 +244,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     // chunk or a 32-element scale block past R reads as zero.
     auto issue_part = [&](const BwdTile& ts, int S, auto PC) {
         constexpr int part = decltype(PC)::value;
+        if constexpr (BF16 && part >= 8) return;  // no scales
         const int lane = lane_of() & 63;
         const uint32_t q = (uint32_t)S & 1;
         const uint32_t kbase = (uint32_t)S * SS_BK;
@@ -305,8 +338,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             const uint32_t o = q * SLOT_BYTES + ((part & 1) ? fb : fa) + (uint32_t)(32 * i * SS_BK);
             const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + (fr ^ (64u * h)));
             const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(lds + o + (fr ^ (64u * h + 32u)));
-            const int sc = (es == 4u) ? *(const __attribute__((address_space(3))) int*)(lds + so)
-                                      : (int)*(const __attribute__((address_space(3))) uint8_t*)(lds + so);
+            int sc = 0;
+            if constexpr (!BF16)
+                sc = (es == 4u) ? *(const __attribute__((address_space(3))) int*)(lds + so)
+                                : (int)*(const __attribute__((address_space(3))) uint8_t*)(lds + so);
             const int8v v = int8v{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
             if (part & 1) { f.b[i] = v; f.sb[i] = sc; } else { f.a[i] = v; f.sa[i] = sc; }
         };
@@ -328,8 +363,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
-                                                                              f.sa[i], 0, f.sb[j]);
+                    acc[i][j] = mfma_step<BF16>(f.a[i], f.b[j], f.sa[i], f.sb[j], acc[i][j]);
         };
         // k step t (fragments in cur) with t even: both halves of its
         // super-stage are in LDS; the MFMAs of t run with the reads of t+1.
@@ -338,8 +372,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const int i = k >> 2, j = k & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cf.a[i], cf.b[j], acc[i][j], 0, 0, 0,
-                                                                          cf.sa[i], 0, cf.sb[j]);
+                acc[i][j] = mfma_step<BF16>(cf.a[i], cf.b[j], cf.sa[i], cf.sb[j], acc[i][j]);
                 if (k >= 2 && k < 10) read_part(t + 1, nf, k - 2);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -356,8 +389,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 const int i = k >> 2, j = k & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cf.a[i], cf.b[j], acc[i][j], 0, 0, 0,
-                                                                          cf.sa[i], 0, cf.sb[j]);
+                acc[i][j] = mfma_step<BF16>(cf.a[i], cf.b[j], cf.sa[i], cf.sb[j], acc[i][j]);
                 switch (k) {
                     case 0: issue_part(cur, S, IC<0>{}); break;
                     case 1: issue_part(cur, S, IC<1>{}); break;
@@ -534,10 +566,12 @@ hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s) {
     static bool attr_set = false;  // idempotent; racing writers set the same value
     const int lds_max = (int)(sizeof(BwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E));
     if (!attr_set) {
-        const void* ks[4] = {reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, true>),
-                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false>),
-                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, true>),
-                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false>)};
+        const void* ks[6] = {reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, true, false>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false, false>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, true, false>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false, false>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false, true>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false, true>)};
         for (const void* k : ks) {
             err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
             if (err != hipSuccess) return err;
@@ -545,17 +579,26 @@ hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s) {
         attr_set = true;
     }
     const size_t lds = sizeof(BwdSmem) + lds_table_bytes(args.E);
-    if (args.out_f32) {
-        if (args.wgrad)
-            hipLaunchKernelGGL((k_gemm_bwd_mxfp8<true, true>), dim3(grid), dim3(256), lds, s, args);
+#define BSQ_GEMM_LAUNCH(F32, WG, B16) \
+    hipLaunchKernelGGL((k_gemm_bwd_mxfp8<F32, WG, B16>), dim3(grid), dim3(256), lds, s, args)
+    if (args.bf16) {
+        if (args.wgrad) return hipErrorInvalidValue;  // not a bf16 mode
+        if (args.out_f32)
+            BSQ_GEMM_LAUNCH(true, false, true);
         else
-            hipLaunchKernelGGL((k_gemm_bwd_mxfp8<true, false>), dim3(grid), dim3(256), lds, s, args);
+            BSQ_GEMM_LAUNCH(false, false, true);
+    } else if (args.out_f32) {
+        if (args.wgrad)
+            BSQ_GEMM_LAUNCH(true, true, false);
+        else
+            BSQ_GEMM_LAUNCH(true, false, false);
     } else {
         if (args.wgrad)
-            hipLaunchKernelGGL((k_gemm_bwd_mxfp8<false, true>), dim3(grid), dim3(256), lds, s, args);
+            BSQ_GEMM_LAUNCH(false, true, false);
         else
-            hipLaunchKernelGGL((k_gemm_bwd_mxfp8<false, false>), dim3(grid), dim3(256), lds, s, args);
+            BSQ_GEMM_LAUNCH(false, false, false);
     }
+#undef BSQ_GEMM_LAUNCH
     return hipGetLastError();
 }
 

@@ -156,6 +156,9 @@ struct BwdArgs {
     // W [E*K][N] with block-major scales [N/32][E*K] (the forward MXFP8 GEMM,
     // whose reduction is N here and whose output width is K).
     int b_rows;
+    // 1: plain bf16 operands (the bf16 baseline), dgrad-style tiles with B as
+    // a row-major weight stack (b_rows layout, 2 bytes per element, no scales)
+    int bf16;
 };
 
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t m_total, int mode, int bm, int nt, int kt,

@@ -249,6 +249,24 @@ bsq_status bsq_grouped_gemm_fwd_mxfp8(const uint8_t* x_codes, const uint8_t* x_s
                                       int64_t k, void* y, bsq_dtype y_dtype, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * bsq_grouped_gemm_bf16 -- the bf16 baseline of the forward expert grouped
+ * GEMM: y[m][j] = sum_k x[m][k] * W_e[j][k] for every row m of expert e's
+ * segment, on plain bf16 operands with the same tiles, DMA pipeline and tile
+ * scheduler as the block-scaled kernels ("Scaling and Optimizing Frontier
+ * Model Training", MXFP8 expert kernels: the block-scaled grouped GEMMs are
+ * measured against BF16 on the 32-expert, 7168/2048 shapes).  bf16 MFMA,
+ * fp32 accumulation in a fixed order per element.
+ *   x_bf16 [m_total][k], w_bf16 [num_experts*n][k] (rows e*n + j), row-major,
+ *   16-byte aligned; y [m_total][n] in y_dtype.
+ *   n % 64 == 0, k % 64 == 0, num_experts >= 1; workspace as for
+ *   bsq_grouped_gemm_fwd (BSQ_OP_GEMM_FWD).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP.
+ */
+bsq_status bsq_grouped_gemm_bf16(const void* x_bf16, const void* w_bf16, const int32_t* offsets,
+                                 int32_t num_experts, int64_t m_total, int64_t n, int64_t k, void* y,
+                                 bsq_dtype y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace the GEMM entry points need (host function, no GPU use).
  * op is BSQ_OP_GEMM_FWD or BSQ_OP_GEMM_BWD; returns 0 for invalid arguments. */
 size_t bsq_workspace_size(int op, int32_t num_experts, int64_t m_total, int64_t n, int64_t k);

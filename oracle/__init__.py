@@ -295,6 +295,25 @@ def grouped_gemm_fwd_mxfp8(x_q, w_q, offsets, rows=None, absolute=False) -> np.n
     return y
 
 
+def grouped_gemm_bf16(x_bf16, w_bf16, offsets, rows=None) -> np.ndarray:
+    """bf16 baseline of the forward expert GEMM ("Scaling and Optimizing
+    Frontier Model Training", MXFP8 expert kernels, compared with BF16), in
+    float64: Y[m, j] = sum_k X[m, k] * W_e[j, k] for m in segment e, with the
+    bf16 inputs taken exactly."""
+    x, w = _bf16(x_bf16), _bf16(w_bf16)
+    off = np.asarray(offsets, np.int64)
+    E = len(off) - 1
+    N = w.shape[0] // E
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows, np.int64)
+    exp_of = _expert_of_rows(off, rows)
+    y = np.zeros((len(rows), N), np.float64)
+    f64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for e in np.unique(exp_of):
+        sel = np.nonzero(exp_of == e)[0]
+        y[sel] = f64(x[rows[sel]]) @ f64(w[int(e) * N:(int(e) + 1) * N]).T
+    return y
+
+
 def grouped_gemm_dgrad(dy_q, wt_q, offsets, n, rows=None, absolute=False) -> np.ndarray:
     """dX[m, k] = sum_n dY_hat[m, n] * W_hat_e[n, k] (float64).
 

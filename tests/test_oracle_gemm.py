@@ -220,6 +220,31 @@ def test_fwd_mxfp8_matches_exact_blocks(orc):
     assert np.array_equal(orc.grouped_gemm_fwd_mxfp8(x_q, w_q, off, rows=rows), y[rows])
 
 
+def test_bf16_gemm_exact_on_integers_and_rationals(orc):
+    """bf16 baseline: small-integer operands give exact int64 sums; a tiny
+    case against exact rationals; rows follow their expert's weights."""
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(29)
+    counts = [5, 0, 12, 3]
+    E, n, k = len(counts), 8, 96
+    off = offsets_from_counts(counts)
+    M = int(off[-1])
+    xi = rng.integers(-16, 17, (M, k))
+    wi = rng.integers(-16, 17, (E * n, k))
+    y = orc.grouped_gemm_bf16(f32_to_bf16_bits(xi.astype(np.float32)), f32_to_bf16_bits(wi.astype(np.float32)), off)
+    for e in range(E):
+        m0, m1 = int(off[e]), int(off[e + 1])
+        assert np.array_equal(y[m0:m1], (xi[m0:m1] @ wi[e * n:(e + 1) * n].T).astype(np.float64))
+    xb = normal_bf16(rng, (3, 5))
+    wb = normal_bf16(rng, (2, 5))
+    yb = orc.grouped_gemm_bf16(xb, wb, np.array([0, 3], np.int32))
+    xv, wv = bf16_bits_to_f32(xb), bf16_bits_to_f32(wb)
+    for m in range(3):
+        for j in range(2):
+            exact = sum(Fraction(float(xv[m, q])) * Fraction(float(wv[j, q])) for q in range(5))
+            assert abs(Fraction(yb[m, j]) - exact) <= abs(exact) * Fraction(1, 10 ** 14)
+
+
 def test_single_expert_is_dense(orc):
     """With offsets [0, M] the grouped fwd equals one dense product of the
     dequantized matrices, and dequantized values are the bf16 inputs to
