@@ -395,26 +395,48 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
     const int pr = t & 63, b = t >> 6;  // channel pair, block (one block per wave)
     const int64_t pc = p0 + 32 * b;
     const int c = c_base + 2 * pr;
-    if (pc >= P || c >= cols) return;
-    uint32_t w0[16], w1[16];
+    const bool active = pc < P && c < cols;
+    MxBlock e0, e1;
+    if (active) {
+        uint32_t w0[16], w1[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const uint32_t r0 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j) * 256 + 4 * pr]);
-        const uint32_t r1 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j + 1) * 256 + 4 * pr]);
-        w0[j] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // low halves: channel 2p, tokens 2j, 2j+1
-        w1[j] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // high halves: channel 2p+1
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t r0 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j) * 256 + 4 * pr]);
+            const uint32_t r1 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j + 1) * 256 + 4 * pr]);
+            w0[j] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // low halves: channel 2p, tokens 2j, 2j+1
+            w1[j] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // high halves: channel 2p+1
+        }
+        e0 = mx_encode(w0);
+        e1 = mx_encode(w1);
+        uint8_t* sp = scale + (pc >> 5) * cols + c;  // block-major: coalesced across channels
+        sp[0] = (uint8_t)e0.sbyte;
+        sp[1] = (uint8_t)e1.sbyte;
     }
-    const MxBlock e0 = mx_encode(w0);
-    const MxBlock e1 = mx_encode(w1);
-    uint4* o0 = reinterpret_cast<uint4*>(codes + (int64_t)c * P + pc);
-    uint4* o1 = reinterpret_cast<uint4*>(codes + (int64_t)(c + 1) * P + pc);
-    o0[0] = e0.c0;
-    o0[1] = e0.c1;
-    o1[0] = e1.c0;
-    o1[1] = e1.c1;
-    uint8_t* sp = scale + (pc >> 5) * cols + c;  // block-major: coalesced across channels
-    sp[0] = (uint8_t)e0.sbyte;
-    sp[1] = (uint8_t)e1.sbyte;
+    // The codes leave through LDS as whole 128-byte rows (one channel, the
+    // tile's 128 tokens): output row r keeps its eight 16-byte chunks at
+    // chunk ^ ((r >> 1) & 7), which spreads the eight rows a group of lanes
+    // writes (rows 2p, p = 8k .. 8k+7) over all banks.
+    __syncthreads();  // every wave is done reading the input tile
+    uint8_t* otile = tile;
+    if (active) {
+        const int r0 = 2 * pr;
+        const int sw = pr & 7;  // (r >> 1) & 7 for rows 2p and 2p+1
+        *reinterpret_cast<uint4*>(&otile[r0 * 128 + (((2 * b) ^ sw) * 16)]) = e0.c0;
+        *reinterpret_cast<uint4*>(&otile[r0 * 128 + (((2 * b + 1) ^ sw) * 16)]) = e0.c1;
+        *reinterpret_cast<uint4*>(&otile[(r0 + 1) * 128 + (((2 * b) ^ sw) * 16)]) = e1.c0;
+        *reinterpret_cast<uint4*>(&otile[(r0 + 1) * 128 + (((2 * b + 1) ^ sw) * 16)]) = e1.c1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int id = it * 256 + t;         // 128 rows x 8 chunks
+        const int r = id >> 3, part = id & 7;
+        const int64_t pp = p0 + 16 * part;   // first token of the chunk
+        if (pp < P && c_base + r < cols) {
+            const uint4 v = *reinterpret_cast<const uint4*>(&otile[r * 128 + ((part ^ ((r >> 1) & 7)) * 16)]);
+            *reinterpret_cast<uint4*>(codes + (int64_t)(c_base + r) * P + pp) = v;
+        }
+    }
 }
 
 // ------------------------------------------------------- debug encoders
