@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
 
     auto setup = [&](int tl) -> BwdTile {
         const int lane = lane_of() & 63;
-        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tl);
+        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tl, lane);
         const int e = tr.e;
         const int64_t off0 = tr.off0, off1 = tr.off1;
         const uint8_t *a, *as, *b, *bs;

@@ -127,9 +127,35 @@ __device__ __forceinline__ void fill_lds_tables(__attribute__((address_space(3))
     }
 }
 
+// Wave-parallel decode from the LDS tables: each round reads 64 consecutive
+// tile starts (one per lane) and counts those <= t; the starts never
+// decrease, so the counted entries are a prefix and the last of them is the
+// expert position (one round for up to 64 experts).
+__device__ __forceinline__ TileRef decode_tile_lds(lds_i32p start, lds_i32p order, lds_i32p offs, int E, int t,
+                                                   int lane) {
+    int pos = 0, s_pos = 0;
+    for (int base = 0; base < E; base += 64) {
+        const int i = base + lane;
+        const int st = i < E ? start[i] : 0x7FFFFFFF;
+        const int c = __builtin_popcountll(__ballot(st <= t));
+        if (c > 0) {
+            pos = base + c - 1;
+            s_pos = __builtin_amdgcn_readlane(st, c - 1);
+        }
+        if (c < 64) break;
+    }
+    TileRef r;
+    r.e = __builtin_amdgcn_readfirstlane(order[pos]);
+    r.local = __builtin_amdgcn_readfirstlane(t - s_pos);
+    r.off0 = __builtin_amdgcn_readfirstlane(offs[r.e]);
+    r.off1 = __builtin_amdgcn_readfirstlane(offs[r.e + 1]);
+    return r;
+}
+
 __device__ __forceinline__ TileRef decode_tile_any(bool in_lds, const __attribute__((address_space(3))) int32_t* tab,
-                                                   const int32_t* plan, const int32_t* offsets, int E, int t) {
-    if (in_lds) return decode_tile<lds_i32p>(tab, tab + E + 1, tab + 2 * E + 1, E, t);
+                                                   const int32_t* plan, const int32_t* offsets, int E, int t,
+                                                   int lane) {
+    if (in_lds) return decode_tile_lds(tab, tab + E + 1, tab + 2 * E + 1, E, t, lane);
     return decode_tile<const int32_t*>(plan_start(plan), plan_order(plan, E), offsets, E, t);
 }
 

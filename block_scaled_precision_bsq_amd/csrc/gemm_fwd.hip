@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
         int next_tile = 0;
         if (tid == 0) next_tile = claim_tile(p.plan, xcd, total, dq);
 
-        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tile);
+        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tile, lane);
         const int e = tr.e;
         const int local = tr.local;
         const int64_t off0 = tr.off0;

@@ -292,6 +292,18 @@ def test_bwd_full_size_sampled(orc, bsq_gpu, cfg_id):
         check_groups(got, ref, [(("wgrad", e), np.arange(len(nrows)))], strict=False, absum=absum)
 
 
+@pytest.mark.parametrize("E", [200, 900])
+def test_many_experts(orc, bsq_gpu, E):
+    """Many small experts, a third of them empty: 200 experts decode through
+    several wave-wide rounds of the LDS tables, 900 exceed the LDS tables and
+    decode from the planner's arrays in global memory."""
+    rng = rng_for(7, salt=E)
+    counts = rng.integers(0, 24, E)
+    counts[rng.random(E) < 0.33] = 0
+    _fwd_case(orc, bsq_gpu, list(counts), 64, 128, seed=E)
+    _bwd_case(orc, bsq_gpu, list(counts), 64, 128, seed=E + 1)
+
+
 def test_invalid_offsets_reported(bsq_gpu):
     """Decreasing offsets: the planner flags them and no tile runs."""
     off = _to_dev(np.array([0, 50, 40, 64], np.int32))
