@@ -287,6 +287,29 @@ def quantize_config2(bsq, torch, dev, reps=20):
         us = a.elapsed_time(b) * 1e3 / reps
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 2), "bytes": nbytes, "gbps": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_GBS, 4)}
+    # Dispatch-style quantize: 4096 tokens of the same data, top-8 routing into
+    # 32768 expert-sorted slots, permutation fused into the MXFP8 quantizer.
+    T, k = 4096, 8
+    picks = torch.argsort(torch.rand((T, 32), generator=gen, device=dev), dim=1)[:, :k]
+    idx = (torch.argsort(picks.reshape(-1), stable=True) // k).to(torch.int32)
+    gc = torch.empty((T * k, C), dtype=torch.uint8, device=dev)
+    gs = torch.empty((C // 32, T * k), dtype=torch.uint8, device=dev)
+    xs = x[:T]
+    for _ in range(3):
+        bsq.bsq_quantize_mxfp8_gather(xs, idx, codes=gc, scale=gs)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        bsq.bsq_quantize_mxfp8_gather(xs, idx, codes=gc, scale=gs)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    nbytes = 2 * T * k * C + T * k * C + T * k * C // 32   # gathered bf16 rows read + codes + scales
+    nmin = 2 * T * C + T * k * C + T * k * C // 32         # each source row once + codes + scales
+    out["mxfp8_gather_dispatch"] = {"workload": "4096 tokens x 7168, top-8 into 32768 expert-sorted slots",
+                                    "us": round(us, 2), "bytes_gathered": nbytes,
+                                    "gbps_gathered": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes_min": nmin,
+                                    "gbps_min": round(nmin / (us * 1e-6) / 1e9, 1)}
     # Ablation (not the method): the same quantizer with fast approximate
     # divides; how many decisions it changes against IEEE division, and its time.
     bsq.bsq_quantize_nvfp4v(x, *nv)

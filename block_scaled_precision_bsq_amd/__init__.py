@@ -36,6 +36,7 @@ BSQ_OP_GEMM_FWD, BSQ_OP_GEMM_BWD = 0, 1
 _SIGS = {
     "bsq_quantize_nvfp4v": ([P, I64, I64, I64, P, I32, P, P, P, P], INT),
     "bsq_swiglu_quantize_nvfp4v": ([P, I64, I64, I64, P, I64, P, P, P, P], INT),
+    "bsq_quantize_mxfp8_gather": ([P, I64, I64, I64, P, I64, P, P, P], INT),
     "bsq_debug_quantize_nvfp4v_fastdiv": ([P, I64, I64, I64, P, P, P, P], INT),
     "bsq_quantize_mxfp8": ([P, I64, I64, I64, INT, P, I32, P, P, P], INT),
     "bsq_grouped_gemm_fwd": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
@@ -142,6 +143,26 @@ def bsq_debug_quantize_nvfp4v_fastdiv(x, stream=None):
            _lib.bsq_debug_quantize_nvfp4v_fastdiv(_ptr(x), rows, cols, ld, _ptr(codes), _ptr(bscale), _ptr(rscale),
                                                   _stream(stream)))
     return codes, bscale, rscale
+
+
+def bsq_quantize_mxfp8_gather(x, row_index, codes=None, scale=None, stream=None):
+    """MXFP8 ROWWISE quantization of the rows ``x[row_index]`` (int32 device
+    indices; out-of-range indices give zero rows) in one pass.
+    Returns (codes [rows, cols], scale [cols/32, rows])."""
+    _dev(x, "x", _BF16)
+    _dev(row_index, "row_index", (torch.int32,))
+    src_rows, cols, ld = _rows_ld(x)
+    rows = row_index.numel()
+    dev = x.device
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if codes is None else codes
+    scale = torch.empty((cols // 32, rows), dtype=torch.uint8, device=dev) if scale is None else scale
+    for t, nm, shape in ((codes, "codes", (rows, cols)), (scale, "scale", (cols // 32, rows))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous with shape {shape}")
+    _check("bsq_quantize_mxfp8_gather",
+           _lib.bsq_quantize_mxfp8_gather(_ptr(x), src_rows, cols, ld, _ptr(row_index), rows, _ptr(codes),
+                                          _ptr(scale), _stream(stream)))
+    return codes, scale
 
 
 def bsq_swiglu_quantize_nvfp4v(gu, h=None, write_h=True, codes=None, bscale=None, rscale=None, stream=None):

@@ -14,6 +14,8 @@ namespace bsq {
 hipError_t launch_quantize_nvfp4v(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, float*, hipStream_t);
 hipError_t launch_swiglu_quantize_nvfp4v(const uint16_t*, int64_t, int, int64_t, uint16_t*, int64_t, uint8_t*, uint8_t*,
                                          float*, hipStream_t);
+hipError_t launch_quantize_mxfp8_gather(const uint16_t*, int64_t, int, int64_t, const int32_t*, int64_t, uint8_t*,
+                                        uint8_t*, hipStream_t);
 hipError_t launch_quantize_nvfp4v_fastdiv(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, float*,
                                           hipStream_t);
 hipError_t launch_quantize_mxfp8_rowwise(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, hipStream_t);
@@ -103,6 +105,19 @@ bsq_status bsq_debug_quantize_nvfp4v_fastdiv(const void* x_bf16, int64_t rows, i
     if (rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
     return from_hip(bsq::launch_quantize_nvfp4v_fastdiv(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x,
                                                         codes, bscale, rscale, stream));
+}
+
+bsq_status bsq_quantize_mxfp8_gather(const void* x_bf16, int64_t src_rows, int64_t cols, int64_t ld_x,
+                                    const int32_t* row_index, int64_t rows, uint8_t* codes, uint8_t* scale,
+                                    hipStream_t stream) {
+    if (src_rows < 0 || cols < 0 || rows < 0) return BSQ_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return BSQ_OK;
+    if (!row_index || !codes || !scale || (src_rows > 0 && !x_bf16) || ld_x < cols) return BSQ_ERR_INVALID_ARG;
+    if (cols % 32 || ld_x % 8 || (x_bf16 && !aligned(x_bf16, 16)) || !aligned(codes, 16)) return BSQ_ERR_UNSUPPORTED;
+    // source offsets are 32-bit: src_rows * ld_x * 2 bytes must stay below 2^31
+    if (src_rows * ld_x * 2 >= kMaxBufferOffset || rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
+    return from_hip(bsq::launch_quantize_mxfp8_gather(static_cast<const uint16_t*>(x_bf16), src_rows, (int)cols, ld_x,
+                                                      row_index, rows, codes, scale, stream));
 }
 
 bsq_status bsq_swiglu_quantize_nvfp4v(const void* gu_bf16, int64_t rows, int64_t inter, int64_t ld_gu, void* h_bf16,

@@ -225,11 +225,16 @@ constexpr int MXR_ROWS = 128;
 constexpr int MXR_BLK = 32;
 constexpr int MXR_PITCH = MXR_ROWS + 8;  // bytes per block row in LDS (bank spread)
 
-template <bool ALIGNED16>
+// GATHER: output row r quantizes source row row_index[r] of x (src_rows
+// rows): the token permutation of an expert dispatch fused into the
+// quantizer; an index outside [0, src_rows) reads as a zero row.
+template <bool ALIGNED16, bool GATHER>
 __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* __restrict__ x, int64_t rows,
                                                                 int cols, int64_t ldx,
                                                                 uint8_t* __restrict__ codes,
-                                                                uint8_t* __restrict__ scale) {
+                                                                uint8_t* __restrict__ scale,
+                                                                const int32_t* __restrict__ row_index,
+                                                                int64_t src_rows) {
     __shared__ __align__(16) uint8_t sb[MXR_BLK * MXR_PITCH];
     const int nb = cols >> 5;
     const int nbt = (nb + MXR_BLK - 1) / MXR_BLK;
@@ -241,7 +246,9 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* 
     // Row offsets are relative to the tile's first row: 128 * ldx * 2 bytes
     // stay below 2^31 (host check).  Rows past the end and blocks past the
     // row read as zero and are not stored.
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(uniform_ptr(x + r0 * ldx), 0x7FFFFFFFu);
+    // (GATHER: offsets from x itself, src_rows * ldx * 2 < 2^31 by a host check)
+    const __amdgpu_buffer_rsrc_t rx = GATHER ? make_rsrc(x, (uint32_t)(src_rows * ldx * 2))
+                                             : make_rsrc(uniform_ptr(x + r0 * ldx), 0x7FFFFFFFu);
     const bool okb = b < nb;
 #pragma unroll 1
     for (int it = 0; it < MXR_ROWS / 8; it += 4) {
@@ -250,8 +257,15 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* 
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int rl = 8 * (it + u) + (t >> 5);
-            const bool ok = okb & (r0 + rl < rows);
-            const uint32_t off = (uint32_t)(((int64_t)rl * ldx + 32 * b) * 2);
+            bool ok = okb & (r0 + rl < rows);
+            uint32_t off;
+            if constexpr (GATHER) {
+                const int64_t src = ok ? (int64_t)row_index[r0 + rl] : -1;
+                ok &= (src >= 0) & (src < src_rows);
+                off = (uint32_t)((src * ldx + 32 * b) * 2);
+            } else {
+                off = (uint32_t)(((int64_t)rl * ldx + 32 * b) * 2);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint4 v = buf_load16(rx, ok ? off + 16u * q : OOB);
@@ -493,19 +507,31 @@ hipError_t launch_swiglu_quantize_nvfp4v(const uint16_t* gu, int64_t rows, int i
     return launch_nvfp4v<true>(gu, rows, inter, ldgu, codes, bscale, rscale, h, ldh, s);
 }
 
-hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
-                                         uint8_t* scale, hipStream_t s) {
+template <bool GATHER>
+static hipError_t launch_mxfp8_rowwise(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
+                                       uint8_t* scale, const int32_t* row_index, int64_t src_rows, hipStream_t s) {
     const int nbt = (cols / 32 + MXR_BLK - 1) / MXR_BLK;
     const int64_t nwg = ((rows + MXR_ROWS - 1) / MXR_ROWS) * nbt;
     if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const bool a16 = (rows % 16 == 0) && ((reinterpret_cast<uintptr_t>(scale) & 15) == 0);
     if (a16)
-        hipLaunchKernelGGL(k_quantize_mxfp8_rowwise<true>, dim3((unsigned)nwg), dim3(256), 0, s, x, rows, cols, ldx,
-                           codes, scale);
+        hipLaunchKernelGGL((k_quantize_mxfp8_rowwise<true, GATHER>), dim3((unsigned)nwg), dim3(256), 0, s, x, rows,
+                           cols, ldx, codes, scale, row_index, src_rows);
     else
-        hipLaunchKernelGGL(k_quantize_mxfp8_rowwise<false>, dim3((unsigned)nwg), dim3(256), 0, s, x, rows, cols, ldx,
-                           codes, scale);
+        hipLaunchKernelGGL((k_quantize_mxfp8_rowwise<false, GATHER>), dim3((unsigned)nwg), dim3(256), 0, s, x, rows,
+                           cols, ldx, codes, scale, row_index, src_rows);
     return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
+                                         uint8_t* scale, hipStream_t s) {
+    return launch_mxfp8_rowwise<false>(x, rows, cols, ldx, codes, scale, nullptr, 0, s);
+}
+
+hipError_t launch_quantize_mxfp8_gather(const uint16_t* x, int64_t src_rows, int cols, int64_t ldx,
+                                        const int32_t* row_index, int64_t rows, uint8_t* codes, uint8_t* scale,
+                                        hipStream_t s) {
+    return launch_mxfp8_rowwise<true>(x, rows, cols, ldx, codes, scale, row_index, src_rows, s);
 }
 
 hipError_t launch_quantize_mxfp8_colwise_t(const uint16_t* x, int64_t rows, int cols, int64_t ldx,

@@ -112,6 +112,27 @@ bsq_status bsq_quantize_nvfp4v(const void* x_bf16, int64_t rows, int64_t cols, i
                                uint8_t* codes, uint8_t* bscale, float* rscale, hipStream_t stream);
 
 /*
+ * bsq_quantize_mxfp8_gather -- MXFP8 ROWWISE quantization fused with the
+ * token permutation of an expert dispatch: output row i is the quantization
+ * of source row row_index[i] ("Composer 2 Technical Report", section 6.1,
+ * and "Cursor Composer 2 report deep dive", section 2: tokens are quantized
+ * to MXFP8 before the expert-parallel dispatch, since the experts compute in
+ * MXFP8 anyway; this is the one-GPU half, the permute into expert-sorted
+ * order, with top-k duplicates as repeated indices).
+ *   x_bf16 [src_rows][ld_x] bf16, 16-byte aligned, ld_x % 8 == 0,
+ *   ld_x >= cols, src_rows * ld_x * 2 < 2^31; cols % 32 == 0.
+ *   row_index [rows] int32 (device): an index outside [0, src_rows) gives an
+ *   all-zero output row (codes 0, scale bytes 0).
+ *   codes [rows][cols] (16-byte aligned), scale [cols/32][rows] block-major:
+ *   the bytes bsq_quantize_mxfp8(BSQ_ROWWISE) gives for the gathered rows.
+ * Errors: INVALID_ARG, UNSUPPORTED (cols multiple, alignment, source size),
+ *   HIP.
+ */
+bsq_status bsq_quantize_mxfp8_gather(const void* x_bf16, int64_t src_rows, int64_t cols, int64_t ld_x,
+                                    const int32_t* row_index, int64_t rows, uint8_t* codes, uint8_t* scale,
+                                    hipStream_t stream);
+
+/*
  * bsq_swiglu_quantize_nvfp4v -- the activation between the two forward
  * expert GEMMs fused with the NVFP4-variant quantization of its output, so
  * the down projection's input is quantized without another pass over H

@@ -195,6 +195,19 @@ def nvfp4v_decision_margins(x_bf16: np.ndarray, delta: float):
     return blocks, elems
 
 
+def quantize_mxfp8_gather(x_bf16: np.ndarray, row_index):
+    """MXFP8 ROWWISE of the rows x[row_index] (the token permutation of an
+    expert dispatch; "Composer 2 Technical Report" section 6.1, tokens
+    quantized to MXFP8 before dispatch).  An index outside [0, rows) stands
+    for an all-zero row."""
+    x = _bf16(x_bf16)
+    idx = np.asarray(row_index, np.int64)
+    ok = (idx >= 0) & (idx < x.shape[0])
+    g = np.zeros((len(idx), x.shape[1]), np.uint16)
+    g[ok] = x[idx[ok]]
+    return quantize_mxfp8_rowwise(g)
+
+
 def padded_cols(ngroups: int, rows: int) -> int:
     return int(lib().orc_colwise_padded_cols(ngroups, rows))
 

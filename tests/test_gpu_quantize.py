@@ -234,3 +234,34 @@ def test_mxfp8_colwise_t_full_size_sampled(orc, bsq_gpu):
     gcn = _np(gc[torch.from_numpy(ch).cuda()])
     gsn = _np(gs[:, torch.from_numpy(ch).cuda()])
     assert np.array_equal(rc, gcn) and np.array_equal(rs, gsn)
+
+
+@pytest.mark.parametrize("src_rows,rows,cols", [(300, 300, 256), (97, 4 * 97, 1056), (64, 130, 7168)])
+def test_mxfp8_gather_parity(orc, bsq_gpu, src_rows, rows, cols):
+    """Dispatch-style permutation fused into the MXFP8 row-wise quantizer:
+    repeated indices (top-k duplicates), a shuffled order and out-of-range
+    indices (zero rows), against the oracle on the gathered rows."""
+    rng = rng_for(2, salt=src_rows + cols)
+    x = make_quantize_input(rng, src_rows, cols)
+    idx = rng.integers(0, src_rows, rows).astype(np.int32)
+    idx[:3] = [-1, src_rows, 2 ** 31 - 1]
+    ref = orc.quantize_mxfp8_gather(x, idx)
+    got = bsq_gpu.bsq_quantize_mxfp8_gather(_bf16_dev(x), _to_dev(idx))
+    for r, g in zip(ref, got):
+        assert np.array_equal(r, _np(g))
+
+
+def test_mxfp8_gather_full_size_sampled(orc, bsq_gpu):
+    """4096 tokens x 7168 dispatched with top-8 routing into 32768 expert-sorted
+    slots in one launch; sampled output rows checked against the oracle."""
+    rng = rng_for(3, salt=41)
+    T, C, k, E = 4096, 7168, 8, 32
+    x = make_quantize_input(rng, T, C)
+    picks = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    order = np.argsort(picks.reshape(-1), kind="stable")
+    idx = (order // k).astype(np.int32)            # slot -> token, expert-sorted
+    codes, scale = bsq_gpu.bsq_quantize_mxfp8_gather(_bf16_dev(x), _to_dev(idx))
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(T * k - 16, T * k), rng.choice(T * k, 96, replace=False)]))
+    ref = orc.quantize_mxfp8_rowwise(x[idx[rows]])
+    assert np.array_equal(_np(codes)[rows], ref[0])
+    assert np.array_equal(_np(scale)[:, rows], ref[1])

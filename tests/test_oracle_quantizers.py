@@ -278,3 +278,23 @@ def test_decision_margins_flag_exactly_the_boundaries(orc):
     # a value far from every boundary stays safe for a large delta as well
     _, e2 = orc.nvfp4v_decision_margins(bf16(row)[None, :], 2.0 ** -6)
     assert not e2[0, :8].any()
+
+
+def test_mxfp8_gather_is_rowwise_of_gathered_rows(orc):
+    """The gather quantizer equals the row-wise quantizer on the identity
+    index; permuting the index permutes output rows and scale columns; a
+    repeated index repeats the row; out-of-range indices give zero rows."""
+    from workloads import make_quantize_input
+    rng = np.random.default_rng(31)
+    x = make_quantize_input(rng, 40, 96)
+    ident = orc.quantize_mxfp8_gather(x, np.arange(40))
+    plain = orc.quantize_mxfp8_rowwise(x)
+    assert np.array_equal(ident[0], plain[0]) and np.array_equal(ident[1], plain[1])
+    perm = rng.permutation(40)
+    pc, ps = orc.quantize_mxfp8_gather(x, perm)
+    assert np.array_equal(pc, plain[0][perm]) and np.array_equal(ps, plain[1][:, perm])
+    idx = np.array([3, 3, -1, 40, 7])
+    gc, gs = orc.quantize_mxfp8_gather(x, idx)
+    assert np.array_equal(gc[0], gc[1]) and np.array_equal(gc[0], plain[0][3])
+    assert not gc[2].any() and not gc[3].any() and not gs[:, 2].any() and not gs[:, 3].any()
+    assert np.array_equal(gc[4], plain[0][7])
