@@ -341,9 +341,10 @@ __device__ __forceinline__ int colt_find_base(const int32_t* __restrict__ offset
 __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
     const uint16_t* __restrict__ x, int64_t rows, int cols, int64_t ldx, const int32_t* __restrict__ offsets,
     int ngroups, int64_t P, uint8_t* __restrict__ codes, uint8_t* __restrict__ scale) {
+    // exactly 32 KB of LDS, so five workgroups fit a CU
     __shared__ __align__(16) uint8_t tile[COLT_TOK * COLT_CH * 2];
-    __shared__ int64_t blk_m0[4];
-    __shared__ int blk_n[4];
+    int64_t blk_m0[4];
+    int blk_n[4];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -353,10 +354,11 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
     const int64_t p0 = (int64_t)(blockIdx.x / nct) * COLT_TOK;
     const int c_base = (int)(blockIdx.x % nct) * COLT_CH;
 
-    if (wave == 0) {
-        // groups of the 4 blocks lie within g0 .. g0 + 3 (a group spans >= 32
-        // columns); with at most 61 groups the window starting at group 0
-        // holds them all and one round of loads does
+    {
+        // every wave finds the segments of the tile's 4 blocks itself (wave-
+        // uniform results): groups of the 4 blocks lie within g0 .. g0 + 3 (a
+        // group spans >= 32 columns); with at most 61 groups the window
+        // starting at group 0 holds them all and one round of loads does
         const int g0 = ngroups <= 61 ? 0 : __builtin_amdgcn_readfirstlane(colt_find_base(offsets, ngroups, p0, lane));
         const int g = g0 + lane;
         const bool have = g < ngroups;
@@ -370,14 +372,11 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
             const int64_t stk = 32 * ((int64_t)(g0 + k) + __builtin_amdgcn_readlane(of0, k) / 32);
             const int64_t mb = __builtin_amdgcn_readlane(of0, k) + (pc - stk);
             const int64_t end = __builtin_amdgcn_readlane(of1, k);
-            if (lane == 0) {
-                const bool ok = pc < P && mb < end;
-                blk_m0[b] = ok ? mb : 0;
-                blk_n[b] = ok ? (int)min((int64_t)32, end - mb) : 0;
-            }
+            const bool ok = pc < P && mb < end;
+            blk_m0[b] = uniform_i64(ok ? mb : 0);
+            blk_n[b] = __builtin_amdgcn_readfirstlane(ok ? (int)min((int64_t)32, end - mb) : 0);
         }
     }
-    __syncthreads();
 
     // DMA: instruction i of this wave covers tile rows 4 * (8 * wave + i) + lane / 16,
     // 16 bytes (8 channels) per lane.  Offsets are taken from the first token
@@ -396,10 +395,16 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int ins = 8 * wave + i;
-            const int row = 4 * ins + (lane >> 4);
-            const int b = row >> 5, ii = row & 31;
-            const bool ok = (ii < blk_n[b]) & (ch < cols);
-            const uint32_t off = (uint32_t)(((blk_m0[b] - mlo + ii) * ldx + ch) * 2);
+            // tile row 4 * ins + lane / 16 = 32 * wave + ii: block `wave`
+            const int ii = 4 * i + (lane >> 4);
+            int64_t m0w = blk_m0[0];
+            int nw = blk_n[0];
+#pragma unroll
+            for (int q = 1; q < 4; ++q) {
+                if (wave == q) { m0w = blk_m0[q]; nw = blk_n[q]; }
+            }
+            const bool ok = (ii < nw) & (ch < cols);
+            const uint32_t off = (uint32_t)(((m0w - mlo + ii) * ldx + ch) * 2);
             dma16(d, ok ? off : OOB, L + 1024u * (uint32_t)ins);
         }
         wait_vmcnt<0>();
