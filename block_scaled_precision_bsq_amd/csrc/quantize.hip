@@ -61,6 +61,93 @@ __device__ __forceinline__ float rcp_approx(float b) {
     return __builtin_amdgcn_rcpf(b);
 }
 
+// Encode one row whose 16-element blocks lane + 64 i (i < BPL, block < nb)
+// this lane holds in v (16 bf16 each); bmax are the blocks' |x| maxima
+// (bf16 bit patterns) and rmax this lane's maximum over them.  Writes the
+// row's codes cr[cols/2], block scales br[nb] and row scale *rs.
+// Scale byte of a 16-element block with |x| maximum amax_b (bf16 bits) in a
+// row with |x| maximum A > 0: S_b = E4M3_RNE(RN32(448 * a_b / A)).  The
+// numerator and denominator are exact; for a_b > 2^119 both are scaled by
+// 2^-8 to keep 448*a_b finite.
+template <bool FASTDIV>
+__device__ __forceinline__ uint32_t nvfp4v_block_scale(uint32_t amax_b, float A) {
+    const float ab = __uint_as_float(amax_b << 16);
+    float num, den;
+    if (ab <= 0x1p119f) { num = 448.0f * ab; den = A; }
+    else                { num = 1.75f * ab;  den = A * 0x1p-8f; }
+    const float t = FASTDIV ? num * rcp_approx(den) : num / den;  // in [0, 448]
+    return e4m3x4(t, 0.0f, 0.0f, 0.0f) & 0xFFu;
+}
+
+// E2M1 codes (8 bytes) of one 16-element block with scale byte S in a row
+// with decode scale s_row: d_b = RN32(S_b * s_row), code = E2M1(RN32(x / d_b))
+// (all zero when d_b == 0).
+template <bool FASTDIV>
+__device__ __forceinline__ uint2 nvfp4v_block_codes(const uint4 (&v)[2], uint32_t S, float s_row) {
+    const float d = e4m3_value(S) * s_row;
+    uint2 out = make_uint2(0, 0);
+    if (d != 0.0f) {
+        float q[16];
+        const uint32_t w[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+        if constexpr (FASTDIV) {
+            const float r = rcp_approx(d);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                q[2 * j] = bf16_lo(w[j]) * r;
+                q[2 * j + 1] = bf16_hi(w[j]) * r;
+            }
+        } else {
+            const double inv = 1.0 / (double)d;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                q[2 * j] = (float)((double)bf16_lo(w[j]) * inv);
+                q[2 * j + 1] = (float)((double)bf16_hi(w[j]) * inv);
+            }
+        }
+        uint32_t c0 = e2m1x2<0>(0u, q[0], q[1]);
+        c0 = e2m1x2<1>(c0, q[2], q[3]);
+        c0 = e2m1x2<2>(c0, q[4], q[5]);
+        c0 = e2m1x2<3>(c0, q[6], q[7]);
+        uint32_t c1 = e2m1x2<0>(0u, q[8], q[9]);
+        c1 = e2m1x2<1>(c1, q[10], q[11]);
+        c1 = e2m1x2<2>(c1, q[12], q[13]);
+        c1 = e2m1x2<3>(c1, q[14], q[15]);
+        out = make_uint2(c0, c1);
+    }
+    return out;
+}
+
+// The row's decode scale from the wave-wide |x| maximum rmax (bf16 bits):
+// s_row = RN32(A / 2688) (0 for an all-zero row, whose outputs are all zero).
+template <bool FASTDIV>
+__device__ __forceinline__ float nvfp4v_row_scale(uint32_t rmax) {
+    const float A = __uint_as_float(rmax << 16);
+    return rmax == 0 ? 0.0f : (FASTDIV ? A * rcp_approx(2688.0f) : A / 2688.0f);  // IEEE binary32 division
+}
+
+// Encode one row whose 16-element blocks lane + 64 i (i < BPL, block < nb)
+// this lane holds in v (16 bf16 each); bmax are the blocks' |x| maxima
+// (bf16 bit patterns) and rmax this lane's maximum over them.  Writes the
+// row's codes cr[cols/2], block scales br[nb] and row scale *rs.
+template <int BPL, bool FASTDIV>
+__device__ __forceinline__ void nvfp4v_encode_row(const uint4 (&v)[BPL][2], const uint32_t (&bmax)[BPL], uint32_t rmax,
+                                                  int nb, int lane, uint8_t* __restrict__ cr,
+                                                  uint8_t* __restrict__ br, float* __restrict__ rs) {
+    rmax = wave_max_u32(rmax);
+    const float s_row = nvfp4v_row_scale<FASTDIV>(rmax);
+    if (lane == 0) *rs = s_row;
+    const float A = __uint_as_float(rmax << 16);
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+        const int b = lane + 64 * i;
+        if (b >= nb) continue;
+        const uint32_t S = rmax ? nvfp4v_block_scale<FASTDIV>(bmax[i], A) : 0u;
+        br[b] = (uint8_t)S;
+        *reinterpret_cast<uint2*>(cr + 8 * b) = rmax ? nvfp4v_block_codes<FASTDIV>(v[i], S, s_row) : make_uint2(0, 0);
+    }
+}
+
+
 template <int BPL, bool SWIGLU, bool FASTDIV = false>
 __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restrict__ x, int64_t rows,
                                                          int cols, int64_t ldx, uint8_t* __restrict__ codes,
@@ -108,72 +195,9 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restr
         bmax[i] = m;
         rmax = max(rmax, m);
     }
-    rmax = wave_max_u32(rmax);
-
     uint8_t* cr = codes + row * (int64_t)(cols >> 1);
     uint8_t* br = bscale + row * (int64_t)nb;
-    if (rmax == 0) {  // all-zero row: zero scale, zero codes
-#pragma unroll
-        for (int i = 0; i < BPL; ++i) {
-            const int b = lane + 64 * i;
-            if (b < nb) {
-                *reinterpret_cast<uint2*>(cr + 8 * b) = make_uint2(0, 0);
-                br[b] = 0;
-            }
-        }
-        if (lane == 0) rscale[row] = 0.0f;
-        return;
-    }
-    const float A = __uint_as_float(rmax << 16);
-    const float s_row = FASTDIV ? A * rcp_approx(2688.0f) : A / 2688.0f;  // IEEE binary32 division
-    if (lane == 0) rscale[row] = s_row;
-
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-        const int b = lane + 64 * i;
-        if (b >= nb) continue;
-        // t_b = RN32(448 * a_b / A): numerator and denominator exact; for
-        // a_b > 2^119 both are scaled by 2^-8 to keep 448*a_b finite.
-        const float ab = __uint_as_float(bmax[i] << 16);
-        float num, den;
-        if (ab <= 0x1p119f) { num = 448.0f * ab; den = A; }
-        else                { num = 1.75f * ab;  den = A * 0x1p-8f; }
-        const float t = FASTDIV ? num * rcp_approx(den) : num / den;  // in [0, 448]
-        const uint32_t S = e4m3x4(t, 0.0f, 0.0f, 0.0f) & 0xFFu;
-        br[b] = (uint8_t)S;
-        const float d = e4m3_value(S) * s_row;
-        uint2 out = make_uint2(0, 0);
-        if (d != 0.0f) {
-            float q[16];
-            const uint32_t w[8] = {v[i][0].x, v[i][0].y, v[i][0].z, v[i][0].w,
-                                   v[i][1].x, v[i][1].y, v[i][1].z, v[i][1].w};
-            if constexpr (FASTDIV) {
-                const float r = rcp_approx(d);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    q[2 * j] = bf16_lo(w[j]) * r;
-                    q[2 * j + 1] = bf16_hi(w[j]) * r;
-                }
-            } else {
-                const double inv = 1.0 / (double)d;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    q[2 * j] = (float)((double)bf16_lo(w[j]) * inv);
-                    q[2 * j + 1] = (float)((double)bf16_hi(w[j]) * inv);
-                }
-            }
-            uint32_t c0 = e2m1x2<0>(0u, q[0], q[1]);
-            c0 = e2m1x2<1>(c0, q[2], q[3]);
-            c0 = e2m1x2<2>(c0, q[4], q[5]);
-            c0 = e2m1x2<3>(c0, q[6], q[7]);
-            uint32_t c1 = e2m1x2<0>(0u, q[8], q[9]);
-            c1 = e2m1x2<1>(c1, q[10], q[11]);
-            c1 = e2m1x2<2>(c1, q[12], q[13]);
-            c1 = e2m1x2<3>(c1, q[14], q[15]);
-            out = make_uint2(c0, c1);
-        }
-        *reinterpret_cast<uint2*>(cr + 8 * b) = out;
-    }
+    nvfp4v_encode_row<BPL, FASTDIV>(v, bmax, rmax, nb, lane, cr, br, rscale + row);
 }
 
 // ---------------------------------------------------------------- MXFP8
