@@ -141,14 +141,13 @@ def main():
         ("swiglu_quant_nvfp4v_h", lambda: bsq.bsq_swiglu_quantize_nvfp4v(gu, h=h, codes=q_h[0], bscale=q_h[1],
                                                                           rscale=q_h[2])),
         ("gemm_fwd_down", lambda: bsq.bsq_grouped_gemm_fwd(q_h, q_wdn, off, Hd, I, y=y, workspace=ws_f)),
-        ("quant_mxfp8_rowwise", lambda: (bsq.bsq_quantize_mxfp8(dy, R, codes=q_dy[0], scale=q_dy[1]),
-                                         bsq.bsq_quantize_mxfp8(dgu, R, codes=q_dgu[0], scale=q_dgu[1]))),
+        # dY and dGU feed dgrad row-wise and wgrad per expert column: both layouts from one read
+        ("quant_mxfp8_dual", lambda: (bsq.bsq_quantize_mxfp8_dual(dy, off, row=q_dy, t=t_dy),
+                                      bsq.bsq_quantize_mxfp8_dual(dgu, off, row=q_dgu, t=t_dgu))),
         ("quant_mxfp8_colwise_t", lambda: (
             bsq.bsq_quantize_mxfp8(w_dn, C, offsets=woff_dn, codes=t_wdn[0], scale=t_wdn[1]),
             bsq.bsq_quantize_mxfp8(w_gu, C, offsets=woff_gu, codes=t_wgu[0], scale=t_wgu[1]),
-            bsq.bsq_quantize_mxfp8(dy, C, offsets=off, codes=t_dy[0], scale=t_dy[1]),
             bsq.bsq_quantize_mxfp8(h, C, offsets=off, codes=t_h[0], scale=t_h[1]),
-            bsq.bsq_quantize_mxfp8(dgu, C, offsets=off, codes=t_dgu[0], scale=t_dgu[1]),
             bsq.bsq_quantize_mxfp8(x, C, offsets=off, codes=t_x[0], scale=t_x[1]))),
         ("gemm_bwd_dgrad_down", lambda: bsq.bsq_grouped_gemm_bwd(off, M, Hd, I, dy_q=q_dy, wt_q=t_wdn,
                                                                  flags=bsq.BSQ_DGRAD, dx=dh, workspace=ws_b)),
@@ -167,11 +166,11 @@ def main():
     }
     nvb = lambda r, c: 2 * r * c + r * c // 2 + r * c // 16 + 4 * r           # bf16 in + codes + scales + rscale
     mxb = lambda r, c: 2 * r * c + r * c + r * c // 32                       # bf16 in + codes + scales
+    mxd = lambda r, c: 2 * r * c + 2 * (r * c + r * c // 32)                 # one read, two layouts out
     qbytes = {
         "quant_nvfp4v_weights": nvb(E * 2 * I, Hd) + nvb(E * Hd, I), "quant_nvfp4v_x": nvb(M, Hd),
-        "swiglu_quant_nvfp4v_h": 2 * M * 2 * I + nvb(M, I), "quant_mxfp8_rowwise": mxb(M, Hd) + mxb(M, 2 * I),
-        "quant_mxfp8_colwise_t": mxb(E * Hd, I) + mxb(E * 2 * I, Hd) + mxb(M, Hd) + mxb(M, I) + mxb(M, 2 * I)
-        + mxb(M, Hd),
+        "swiglu_quant_nvfp4v_h": 2 * M * 2 * I + nvb(M, I), "quant_mxfp8_dual": mxd(M, Hd) + mxd(M, 2 * I),
+        "quant_mxfp8_colwise_t": mxb(E * Hd, I) + mxb(E * 2 * I, Hd) + mxb(M, I) + mxb(M, Hd),
     }
 
     stream = torch.cuda.current_stream()
@@ -272,6 +271,9 @@ def quantize_config2(bsq, torch, dev, reps=20):
                           2 * R * C + R * C + R * C // 32),
         "mxfp8_colwise_t": (lambda: bsq.bsq_quantize_mxfp8(x, bsq.BSQ_COLWISE_T, offsets=one, codes=mc[0], scale=mc[1]),
                             2 * R * C + C * P + C * P // 32),
+        # both layouts from one read (against the two calls above: one bf16 read saved)
+        "mxfp8_dual": (lambda: bsq.bsq_quantize_mxfp8_dual(x, one, row=mr, t=mc),
+                       2 * R * C + R * C + R * C // 32 + C * P + C * P // 32),
     }
     stream = torch.cuda.current_stream()
     out = {"workload": "quantize: 16384 x 7168 bf16 N(0,1), 72 outlier channels x50"}
@@ -427,7 +429,7 @@ def measured_traffic():
         if rec.get("source") == kernel_source_hash(stage):
             out[stage] = rec["bytes"]
     # multi-launch stages: sum of their launches when all are current
-    for stage in ("quant_nvfp4v_weights", "quant_mxfp8_rowwise", "quant_mxfp8_colwise_t"):
+    for stage in ("quant_nvfp4v_weights", "quant_mxfp8_dual", "quant_mxfp8_colwise_t"):
         parts = [k for k in table.get("stages", {}) if k.startswith(stage + ":")]
         if parts and all(k in out for k in parts):
             out[stage] = sum(out[k] for k in parts)

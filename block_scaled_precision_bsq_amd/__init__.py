@@ -39,6 +39,7 @@ _SIGS = {
     "bsq_quantize_mxfp8_gather": ([P, I64, I64, I64, P, I64, P, P, P], INT),
     "bsq_debug_quantize_nvfp4v_fastdiv": ([P, I64, I64, I64, P, P, P, P], INT),
     "bsq_quantize_mxfp8": ([P, I64, I64, I64, INT, P, I32, P, P, P], INT),
+    "bsq_quantize_mxfp8_dual": ([P, I64, I64, I64, P, I32, P, P, P, P, P], INT),
     "bsq_grouped_gemm_fwd": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_bwd": ([P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, INT, ctypes.c_uint, P,
                               ctypes.c_size_t, P], INT),
@@ -222,6 +223,32 @@ def bsq_quantize_mxfp8(x, axis=BSQ_ROWWISE, offsets=None, codes=None, scale=None
            _lib.bsq_quantize_mxfp8(_ptr(x), rows, cols, ld, axis, _ptr(offsets), ng, _ptr(codes), _ptr(scale),
                                    _stream(stream)))
     return codes, scale
+
+
+def bsq_quantize_mxfp8_dual(x, offsets, row=None, t=None, stream=None):
+    """Both MXFP8 layouts of bf16 ``x`` [rows, cols] from one read: returns
+    ((codes [rows, cols], scale [cols/32, rows]) as ROWWISE,
+     (codes [cols, P], scale [P/32, cols]) as COLWISE_T with int32 ``offsets``)."""
+    _dev(x, "x", _BF16)
+    _dev(offsets, "offsets", (torch.int32,))
+    rows, cols, ld = _rows_ld(x)
+    dev = x.device
+    ng = offsets.numel() - 1
+    Pc = bsq_colwise_padded_cols(ng, rows)
+    shapes = ((rows, cols), (cols // 32, rows), (cols, Pc), (Pc // 32, cols))
+    rc, rs = (None, None) if row is None else row
+    tc, ts = (None, None) if t is None else t
+    outs = []
+    for buf, nm, shape in ((rc, "row codes", shapes[0]), (rs, "row scale", shapes[1]),
+                           (tc, "t codes", shapes[2]), (ts, "t scale", shapes[3])):
+        buf = torch.empty(shape, dtype=torch.uint8, device=dev) if buf is None else buf
+        if tuple(buf.shape) != tuple(shape) or not buf.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous with shape {shape}")
+        outs.append(buf)
+    _check("bsq_quantize_mxfp8_dual",
+           _lib.bsq_quantize_mxfp8_dual(_ptr(x), rows, cols, ld, _ptr(offsets), ng, *[_ptr(o) for o in outs],
+                                        _stream(stream)))
+    return (outs[0], outs[1]), (outs[2], outs[3])
 
 
 def _workspace(op, E, m_total, n, k, workspace, dev):

@@ -21,6 +21,8 @@ hipError_t launch_quantize_nvfp4v_fastdiv(const uint16_t*, int64_t, int, int64_t
 hipError_t launch_quantize_mxfp8_rowwise(const uint16_t*, int64_t, int, int64_t, uint8_t*, uint8_t*, hipStream_t);
 hipError_t launch_quantize_mxfp8_colwise_t(const uint16_t*, int64_t, int, int64_t, const int32_t*, int, int64_t,
                                            uint8_t*, uint8_t*, hipStream_t);
+hipError_t launch_quantize_mxfp8_dual(const uint16_t*, int64_t, int, int64_t, const int32_t*, int, int64_t, uint8_t*,
+                                      uint8_t*, uint8_t*, uint8_t*, hipStream_t);
 hipError_t launch_debug_encode(int, const float*, uint8_t*, int64_t, hipStream_t);
 }  // namespace bsq
 
@@ -163,6 +165,22 @@ bsq_status bsq_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t cols, in
     const int64_t P = bsq_colwise_padded_cols(num_groups, rows);
     return from_hip(bsq::launch_quantize_mxfp8_colwise_t(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x,
                                                          offsets, num_groups, P, codes, scale, stream));
+}
+
+bsq_status bsq_quantize_mxfp8_dual(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                   const int32_t* offsets, int32_t num_groups, uint8_t* row_codes,
+                                   uint8_t* row_scale, uint8_t* t_codes, uint8_t* t_scale, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || num_groups < 1 || !offsets) return BSQ_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0) return BSQ_OK;
+    if (!x_bf16 || ld_x < cols || !row_codes || !row_scale || !t_codes || !t_scale) return BSQ_ERR_INVALID_ARG;
+    if (cols > ((int64_t)1 << 30) || num_groups > (1 << 30)) return BSQ_ERR_UNSUPPORTED;
+    if (cols % 32 || ld_x % 8 || !aligned(x_bf16, 16) || !aligned(row_codes, 16) || !aligned(t_codes, 16))
+        return BSQ_ERR_UNSUPPORTED;
+    if (258 * ld_x >= kMaxBufferOffset) return BSQ_ERR_UNSUPPORTED;
+    const int64_t P = bsq_colwise_padded_cols(num_groups, rows);
+    return from_hip(bsq::launch_quantize_mxfp8_dual(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x,
+                                                    offsets, num_groups, P, t_codes, t_scale, row_codes, row_scale,
+                                                    stream));
 }
 
 bsq_status bsq_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_bscale, const float* a_rscale,

@@ -362,9 +362,20 @@ __device__ __forceinline__ int colt_find_base(const int32_t* __restrict__ offset
     return lo + max(__builtin_popcountll(__ballot(le)) - 1, 0);
 }
 
+// DUAL: the same pass also writes the ROWWISE quantization (blocks of 32
+// channels along each token row, codes rcodes [rows][cols], block-major
+// scales rscale [cols/32][rows]) of the tile's tokens from the LDS tile, so
+// a tensor that needs both layouts is read once.
+//
+// The tile holds token rows of 128 channels (256 bytes); 16-byte chunk k of
+// tile row r sits at chunk position k ^ (r & 15), so both the column reads
+// (one channel pair across rows) and the row reads (16 consecutive rows at
+// one chunk) spread over all banks.
+template <bool DUAL>
 __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
     const uint16_t* __restrict__ x, int64_t rows, int cols, int64_t ldx, const int32_t* __restrict__ offsets,
-    int ngroups, int64_t P, uint8_t* __restrict__ codes, uint8_t* __restrict__ scale) {
+    int ngroups, int64_t P, uint8_t* __restrict__ codes, uint8_t* __restrict__ scale,
+    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscale) {
     // exactly 32 KB of LDS, so five workgroups fit a CU
     __shared__ __align__(16) uint8_t tile[COLT_TOK * COLT_CH * 2];
     int64_t blk_m0[4];
@@ -414,13 +425,13 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
         mlo = uniform_i64(mlo);
         const i32x4 d = make_desc(uniform_ptr(x + mlo * ldx));
         const uint32_t L = __builtin_amdgcn_readfirstlane(lds_addr(tile));
-        const int chunk = lane & 15;
-        const int ch = c_base + 8 * chunk;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int ins = 8 * wave + i;
-            // tile row 4 * ins + lane / 16 = 32 * wave + ii: block `wave`
+            // tile row 4 * ins + lane / 16 = 32 * wave + ii: block `wave`;
+            // the lane's LDS slot lane & 15 receives chunk (lane & 15) ^ (ii & 15)
             const int ii = 4 * i + (lane >> 4);
+            const int ch = c_base + 8 * ((lane & 15) ^ (ii & 15));
             int64_t m0w = blk_m0[0];
             int nw = blk_n[0];
 #pragma unroll
@@ -444,8 +455,11 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
         uint32_t w0[16], w1[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const uint32_t r0 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j) * 256 + 4 * pr]);
-            const uint32_t r1 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j + 1) * 256 + 4 * pr]);
+            // pair pr is dword pr & 3 of logical chunk pr >> 2; rows 2j and 2j+1 of the block
+            const uint32_t o0 = (uint32_t)(((pr >> 2) ^ ((2 * j) & 15)) * 16 + (pr & 3) * 4);
+            const uint32_t o1 = (uint32_t)(((pr >> 2) ^ ((2 * j + 1) & 15)) * 16 + (pr & 3) * 4);
+            const uint32_t r0 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j) * 256 + o0]);
+            const uint32_t r1 = *reinterpret_cast<const uint32_t*>(&tile[(32 * b + 2 * j + 1) * 256 + o1]);
             w0[j] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // low halves: channel 2p, tokens 2j, 2j+1
             w1[j] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // high halves: channel 2p+1
         }
@@ -454,6 +468,40 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
         uint8_t* sp = scale + (pc >> 5) * cols + c;  // block-major: coalesced across channels
         sp[0] = (uint8_t)e0.sbyte;
         sp[1] = (uint8_t)e1.sbyte;
+    }
+    if constexpr (DUAL) {
+        // row blocks: lane l of wave w takes tile row r = 32 w + (l & 31)
+        // (token blk_m0[w] + (l & 31) when the block holds one) and the
+        // 32-channel blocks h, h + 2 with h = l / 32: the two half-waves
+        // write neighbouring 32-byte pieces of a row, and 16 lanes that read
+        // LDS together take 16 rows, so the chunk swizzle keeps them apart
+        const int ii = lane & 31, h = lane >> 5, r = 32 * wave + ii;
+        int64_t m0w = blk_m0[0];
+        int nw = blk_n[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+            if (wave == q) { m0w = blk_m0[q]; nw = blk_n[q]; }
+        }
+        if (ii < nw) {
+            const int64_t m = m0w + ii;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const int cb = h + 2 * jb;
+                const int cc = c_base + 32 * cb;
+                if (cc >= cols) continue;
+                uint32_t wv[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 u = *reinterpret_cast<const uint4*>(&tile[r * 256 + (((4 * cb + q) ^ (r & 15)) * 16)]);
+                    wv[4 * q] = u.x; wv[4 * q + 1] = u.y; wv[4 * q + 2] = u.z; wv[4 * q + 3] = u.w;
+                }
+                const MxBlock eb = mx_encode(wv);
+                uint4* o = reinterpret_cast<uint4*>(rcodes + m * (int64_t)cols + cc);
+                o[0] = eb.c0;
+                o[1] = eb.c1;
+                rscale[(int64_t)(cc >> 5) * rows + m] = (uint8_t)eb.sbyte;
+            }
+        }
     }
     // The codes leave through LDS as whole 128-byte rows (one channel, the
     // tile's 128 tokens): output row r keeps its eight 16-byte chunks at
@@ -569,8 +617,19 @@ hipError_t launch_quantize_mxfp8_colwise_t(const uint16_t* x, int64_t rows, int 
     const int64_t nwg = (int64_t)((cols + COLT_CH - 1) / COLT_CH) * ((P + COLT_TOK - 1) / COLT_TOK);
     if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // beyond the host-checked sizes
     const dim3 grid((unsigned)nwg);
-    hipLaunchKernelGGL(k_quantize_mxfp8_colwise_t, grid, dim3(256), 0, s, x, rows, cols, ldx, offsets, ngroups, P,
-                       codes, scale);
+    hipLaunchKernelGGL(k_quantize_mxfp8_colwise_t<false>, grid, dim3(256), 0, s, x, rows, cols, ldx, offsets,
+                       ngroups, P, codes, scale, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp8_dual(const uint16_t* x, int64_t rows, int cols, int64_t ldx, const int32_t* offsets,
+                                      int ngroups, int64_t P, uint8_t* t_codes, uint8_t* t_scale, uint8_t* r_codes,
+                                      uint8_t* r_scale, hipStream_t s) {
+    const int64_t nwg = (int64_t)((cols + COLT_CH - 1) / COLT_CH) * ((P + COLT_TOK - 1) / COLT_TOK);
+    if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)nwg);
+    hipLaunchKernelGGL(k_quantize_mxfp8_colwise_t<true>, grid, dim3(256), 0, s, x, rows, cols, ldx, offsets,
+                       ngroups, P, t_codes, t_scale, r_codes, r_scale);
     return hipGetLastError();
 }
 

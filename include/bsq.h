@@ -192,6 +192,31 @@ bsq_status bsq_quantize_mxfp8(const void* x_bf16, int64_t rows, int64_t cols, in
                               uint8_t* codes, uint8_t* scale, hipStream_t stream);
 
 /*
+ * bsq_quantize_mxfp8_dual -- both MXFP8 layouts of one bf16 tensor from a
+ * single read ("Composer 2 Technical Report", section 6.1, MXFP8 in the MoE
+ * backward: an activation gradient feeds dgrad along its rows and wgrad
+ * along each expert's token dimension, so it is needed blocked both ways).
+ * Writes exactly the bytes of bsq_quantize_mxfp8(BSQ_ROWWISE) into
+ * row_codes/row_scale and of bsq_quantize_mxfp8(BSQ_COLWISE_T, offsets)
+ * into t_codes/t_scale.
+ *   x_bf16 [rows][ld_x] bf16, 16-byte aligned, ld_x % 8 == 0, ld_x >= cols,
+ *   258 * ld_x * 2 < 2^31; cols % 32 == 0.
+ *   offsets [num_groups + 1] int32 (device), num_groups >= 1, as for
+ *   BSQ_COLWISE_T; every row must lie in some group (offsets[0] == 0,
+ *   offsets[num_groups] == rows) or its ROWWISE bytes are not written.
+ *   row_codes [rows][cols] (16-byte aligned), row_scale [cols/32][rows];
+ *   t_codes [cols][P] (16-byte aligned), t_scale [P/32][cols],
+ *   P = bsq_colwise_padded_cols(num_groups, rows).
+ * rows == 0 or cols == 0: nothing to do.
+ * Errors: INVALID_ARG (null pointers, negative sizes, short ld_x),
+ *   UNSUPPORTED (cols multiple, alignment, sizes), HIP.
+ */
+bsq_status bsq_quantize_mxfp8_dual(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                                  const int32_t* offsets, int32_t num_groups,
+                                  uint8_t* row_codes, uint8_t* row_scale,
+                                  uint8_t* t_codes, uint8_t* t_scale, hipStream_t stream);
+
+/*
  * bsq_grouped_gemm_fwd -- forward expert grouped GEMM over NVFP4v operands
  * ("Composer 2 Technical Report", section 6.1: grouped GEMM of the MoE
  * layer; per-token scale applied in the GEMM epilogue):

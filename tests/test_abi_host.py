@@ -68,6 +68,13 @@ def test_quantize_host_checks(bsq):
     assert m(FAKE, 4, 64, 64, 5, None, 0, FAKE, FAKE, None) == bsq.BSQ_ERR_INVALID_ARG
     assert m(FAKE, 4, 64, 64, bsq.BSQ_COLWISE_T, None, 1, FAKE, FAKE, None) == bsq.BSQ_ERR_INVALID_ARG
     assert m(FAKE, 4, 60, 64, bsq.BSQ_COLWISE_T, FAKE, 1, FAKE, FAKE, None) == bsq.BSQ_ERR_UNSUPPORTED
+    d = L.bsq_quantize_mxfp8_dual
+    assert d(FAKE, 4, 64, 64, None, 1, FAKE, FAKE, FAKE, FAKE, None) == bsq.BSQ_ERR_INVALID_ARG  # no offsets
+    assert d(FAKE, 4, 64, 64, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == bsq.BSQ_ERR_INVALID_ARG  # no groups
+    assert d(FAKE, 4, 48, 48, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None) == bsq.BSQ_ERR_UNSUPPORTED  # cols % 32
+    assert d(FAKE, 4, 64, 32, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None) == bsq.BSQ_ERR_INVALID_ARG  # ld < cols
+    assert d(FAKE, 4, 64, 64, FAKE, 1, None, FAKE, FAKE, FAKE, None) == bsq.BSQ_ERR_INVALID_ARG  # null output
+    assert d(FAKE, 0, 64, 64, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None) == bsq.BSQ_OK              # nothing to do
 
 
 def test_gemm_host_checks(bsq):

@@ -236,6 +236,55 @@ def test_mxfp8_colwise_t_full_size_sampled(orc, bsq_gpu):
     assert np.array_equal(rc, gcn) and np.array_equal(rs, gsn)
 
 
+@pytest.mark.parametrize("counts,cols", [([37, 0, 300, 1, 64, 95, 33], 288), ([0, 0, 70, 0, 0], 96),
+                                         ([1000], 512), ([128] * 4, 256), ([5, 250, 3], 2048)])
+def test_mxfp8_dual_parity(orc, bsq_gpu, counts, cols):
+    """One read, both layouts: the ROWWISE bytes and the per-group COLWISE_T
+    bytes against the oracle's two quantizers, on ragged groups (empty ones,
+    a one-token group, partial 32-blocks), partial channel tiles and the
+    special values of the row-wise test."""
+    rng = rng_for(4, salt=50 + cols + len(counts))
+    off = offsets_from_counts(counts)
+    M = int(off[-1])
+    x = make_quantize_input(rng, M, cols)
+    x[0] = 0
+    x[1, :32] = bf16(np.full(32, 2.0 ** -130))
+    x[2] = bf16(rng.standard_normal(cols) * 2.0 ** 125)
+    x[3] = bf16(rng.standard_normal(cols) * 1e-3)
+    x[4, :32] = bf16(np.array([3.875, -0.0] + [0.5] * 30))
+    (grc, grs), (gtc, gts) = bsq_gpu.bsq_quantize_mxfp8_dual(_bf16_dev(x), _to_dev(off))
+    rc, rs = orc.quantize_mxfp8_rowwise(x)
+    tc, ts = orc.quantize_mxfp8_colwise_t(x, off)
+    assert np.array_equal(rc, _np(grc)), np.argwhere(rc != _np(grc))[:5]
+    assert np.array_equal(rs, _np(grs))
+    assert np.array_equal(tc, _np(gtc)), np.argwhere(tc != _np(gtc))[:5]
+    assert np.array_equal(ts, _np(gts))
+
+
+def test_mxfp8_dual_strided_full_size_sampled(orc, bsq_gpu):
+    """dGU-shaped input at full size (32768 x 4096, Zipf(1.1) over 32 experts)
+    read through a leading dimension wider than the row: sampled rows checked
+    ROWWISE and sampled channels COLWISE_T against the oracle."""
+    from workloads import CONFIGS, moe_counts
+    counts = moe_counts(CONFIGS[4])
+    off = offsets_from_counts(counts)
+    gen = torch.Generator(device="cuda").manual_seed(1005)
+    base = (torch.randn((32768, 4096 + 64), generator=gen, device="cuda") * 1e-3).to(torch.bfloat16)
+    x = base[:, :4096]
+    (grc, grs), (gtc, gts) = bsq_gpu.bsq_quantize_mxfp8_dual(x, _to_dev(off))
+    rng = rng_for(4, salt=8)
+    rows = np.unique(np.concatenate([[0, 32767], off[1:-1] - 1, rng.choice(32768, 60, replace=False)]))
+    rows = rows[(rows >= 0) & (rows < 32768)]
+    x_rows = _np(x[torch.from_numpy(rows).cuda()].contiguous().view(torch.int16)).view(np.uint16)
+    rc, rs = orc.quantize_mxfp8_rowwise(x_rows)
+    assert np.array_equal(rc, _np(grc)[rows]) and np.array_equal(rs, _np(grs)[:, rows])
+    ch = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 24, replace=False)]))
+    x_ch = _np(x[:, torch.from_numpy(ch).cuda()].contiguous().view(torch.int16)).view(np.uint16)
+    tc, ts = orc.quantize_mxfp8_colwise_t(np.ascontiguousarray(x_ch), off)
+    assert np.array_equal(tc, _np(gtc[torch.from_numpy(ch).cuda()]))
+    assert np.array_equal(ts, _np(gts[:, torch.from_numpy(ch).cuda()]))
+
+
 @pytest.mark.parametrize("src_rows,rows,cols", [(300, 300, 256), (97, 4 * 97, 1056), (64, 130, 7168)])
 def test_mxfp8_gather_parity(orc, bsq_gpu, src_rows, rows, cols):
     """Dispatch-style permutation fused into the MXFP8 row-wise quantizer:
