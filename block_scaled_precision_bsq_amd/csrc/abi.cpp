@@ -72,7 +72,7 @@ const char* bsq_status_string(bsq_status s) {
 
 int64_t bsq_colwise_padded_cols(int32_t num_groups, int64_t rows) {
     if (num_groups < 0 || rows < 0) return -1;
-    return 32 * ((int64_t)num_groups + (rows + 31) / 32);
+    return 128 * ((int64_t)num_groups + (rows + 127) / 128);
 }
 
 size_t bsq_workspace_size(int op, int32_t num_experts, int64_t m_total, int64_t n, int64_t k) {

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             int mt, kt;
             grouped_tile(tr.local, (int)((off1 - off0 + BWD_BM - 1) / BWD_BM), KT, mt, kt);
             const int64_t m0 = off0 + (int64_t)mt * BWD_BM, k0 = (int64_t)kt * BWD_BN;
-            const int64_t cw = (int64_t)e * (p.N + 32);  // 32*(e + e*N/32): segment start of W_e
+            const int64_t cw = 128 * ((int64_t)e + (int64_t)e * p.N / 128);  // segment start of W_e
             // block-major scales: block j of rows r0.. starts at base + j * rows_total + r0
             a = p.dy_codes + m0 * p.N; as = p.dy_scale + m0;
             lda = p.N; ldas = p.m_total; rows_a = (int)min((int64_t)BWD_BM, off1 - m0);
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             int nt, kt;
             grouped_tile(tr.local, (int)((p.N + BWD_BM - 1) / BWD_BM), KT, nt, kt);
             const int64_t n0 = (int64_t)nt * BWD_BM, k0 = (int64_t)kt * BWD_BN;
-            const int64_t c0 = 32 * ((int64_t)e + off0 / 32);  // segment start column
+            const int64_t c0 = 128 * ((int64_t)e + off0 / 128);  // segment start column (128-byte aligned)
             a = p.dyt_codes + n0 * p.P + c0; as = p.dyt_scale + (c0 / 32) * p.N + n0;
             lda = p.P; ldas = p.N; rows_a = (int)min((int64_t)BWD_BM, p.N - n0);
             b = p.xt_codes + k0 * p.P + c0; bs = p.xt_scale + (c0 / 32) * p.K + k0;

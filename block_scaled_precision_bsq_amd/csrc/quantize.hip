@@ -330,7 +330,8 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* 
 // Column-transposing MXFP8 per group.  A workgroup owns 128 padded output
 // columns (four 32-blocks of tokens) x 128 channels.  Block b of the tile is
 // padded column range [p0 + 32b, +32) = tokens [m0_b, m0_b + n_b) of one
-// group (n_b < 32 at a group's end, 0 in padding).  The bf16 tile
+// group (n_b < 32 at a group's end, 0 in padding; groups start on multiples
+// of 128 columns, so all four blocks belong to the same group).  The bf16 tile
 // [128 token slots][128 channels] (256-byte rows, 32 KB) arrives through
 // buffer-to-LDS DMA, slots past n_b as zeros.  Thread (pair p, block b) then
 // encodes channels 2p and 2p+1 of block b from 32 dword reads (one token row
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* 
 constexpr int COLT_TOK = 128;
 constexpr int COLT_CH = 128;
 
-// Group of padded column pc: the last g with start(g) = 32 * (g + off[g]/32)
+// Group of padded column pc: the last g with start(g) = 128 * (g + off[g]/128)
 // <= pc (starts strictly increase).  Wave-wide 64-ary search: one round of
 // loads for up to 64 groups.  Returns the group; lane l's (start, off) of
 // group base + l come back through `base`, `st`, `of0`, `of1` for the caller.
@@ -351,14 +352,14 @@ __device__ __forceinline__ int colt_find_base(const int32_t* __restrict__ offset
     while (n > 64) {
         const int step = (n + 63) / 64;
         const int g = lo + lane * step;
-        const bool le = (g < lo + n) && (32 * ((int64_t)g + offsets[g] / 32) <= pc);
+        const bool le = (g < lo + n) && (128 * ((int64_t)g + offsets[g] / 128) <= pc);
         const int cnt = __builtin_popcountll(__ballot(le));
         const int nlo = lo + max(cnt - 1, 0) * step;
         n = min(step, lo + n - nlo);
         lo = nlo;
     }
     const int g = lo + lane;
-    const bool le = (g < lo + n) && (32 * ((int64_t)g + offsets[g] / 32) <= pc);
+    const bool le = (g < lo + n) && (128 * ((int64_t)g + offsets[g] / 128) <= pc);
     return lo + max(__builtin_popcountll(__ballot(le)) - 1, 0);
 }
 
@@ -391,20 +392,21 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
 
     {
         // every wave finds the segments of the tile's 4 blocks itself (wave-
-        // uniform results): groups of the 4 blocks lie within g0 .. g0 + 3 (a
-        // group spans >= 32 columns); with at most 61 groups the window
-        // starting at group 0 holds them all and one round of loads does
+        // uniform results): group starts are multiples of 128, so the 4 blocks
+        // of a tile lie in one group's span, found from p0; with at most 61
+        // groups the window starting at group 0 holds them all and one round
+        // of loads does
         const int g0 = ngroups <= 61 ? 0 : __builtin_amdgcn_readfirstlane(colt_find_base(offsets, ngroups, p0, lane));
         const int g = g0 + lane;
         const bool have = g < ngroups;
         const int32_t of0 = have ? offsets[g] : 0;
         const int32_t of1 = have ? offsets[g + 1] : 0;
-        const int64_t st = 32 * ((int64_t)g + of0 / 32);
+        const int64_t st = 128 * ((int64_t)g + of0 / 128);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int64_t pc = p0 + 32 * b;
             const int k = max(__builtin_popcountll(__ballot(have && st <= pc)) - 1, 0);
-            const int64_t stk = 32 * ((int64_t)(g0 + k) + __builtin_amdgcn_readlane(of0, k) / 32);
+            const int64_t stk = 128 * ((int64_t)(g0 + k) + __builtin_amdgcn_readlane(of0, k) / 128);
             const int64_t mb = __builtin_amdgcn_readlane(of0, k) + (pc - stk);
             const int64_t end = __builtin_amdgcn_readlane(of1, k);
             const bool ok = pc < P && mb < end;

@@ -49,10 +49,12 @@
  *  MXFP8 COLWISE_T of an input [rows][cols] with groups `offsets`:
  *    blocks of 32 run DOWN the rows of each group and restart at each group;
  *    the output is transposed: codes [cols][P], scale [P/32][cols] with
- *    P = bsq_colwise_padded_cols(num_groups, rows) = 32*(num_groups +
- *    ceil(rows/32)).  Group g starts at column c0(g) = 32*(g + offsets[g]/32)
- *    (integer division) and spans 32*ceil(M_g/32) columns; every byte not
- *    holding a real element (tails, gaps, the end) is 0.
+ *    P = bsq_colwise_padded_cols(num_groups, rows) = 128*(num_groups +
+ *    ceil(rows/128)).  Group g starts at column c0(g) = 128*(g +
+ *    offsets[g]/128) (integer division), so every group's code rows begin on
+ *    a 128-byte line (one L2 request per line for the GEMMs), and spans
+ *    32*ceil(M_g/32) columns; every byte not holding a real element (tails,
+ *    gaps, the end) is 0.
  */
 #ifndef BSQ_H_
 #define BSQ_H_
@@ -317,7 +319,7 @@ bsq_status bsq_grouped_gemm_bf16(const void* x_bf16, const void* w_bf16, const i
  * op is BSQ_OP_GEMM_FWD or BSQ_OP_GEMM_BWD; returns 0 for invalid arguments. */
 size_t bsq_workspace_size(int op, int32_t num_experts, int64_t m_total, int64_t n, int64_t k);
 
-/* P of the COLWISE_T layout: 32 * (num_groups + ceil(rows / 32)) (host). */
+/* P of the COLWISE_T layout: 128 * (num_groups + ceil(rows / 128)) (host). */
 int64_t bsq_colwise_padded_cols(int32_t num_groups, int64_t rows);
 
 /* Static description of a status code (host). */

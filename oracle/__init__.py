@@ -214,7 +214,7 @@ def padded_cols(ngroups: int, rows: int) -> int:
 
 def segment_start(g: int, offsets) -> int:
     """First padded column of segment g in the COLWISE_T layout."""
-    return 32 * (g + int(offsets[g]) // 32)
+    return 128 * (g + int(offsets[g]) // 128)
 
 
 def quantize_mxfp8_colwise_t(x_bf16: np.ndarray, offsets):

@@ -42,10 +42,12 @@
  *           R-row matrix is at b * R + r.
  *  COLWISE_T  the MXFP8 blocks run down the rows (tokens) of each segment
  *           [off[g], off[g+1]) and restart at each segment; the output is
- *           transposed, codes [cols][P] with P = 32*(G + ceil(rows/32)),
+ *           transposed, codes [cols][P] with P = 128*(G + ceil(rows/128)),
  *           scales [P/32][cols] (block-major); segment g starts at column
- *           c0[g] = 32*(g + floor(off[g]/32)); every other byte (padding,
- *           gaps) is 0.
+ *           c0[g] = 128*(g + floor(off[g]/128)), a whole 128-byte line of
+ *           every code row; every other byte (padding, gaps) is 0.  This
+ *           padded layout is the library's storage convention; the pages fix
+ *           only the element format and the 32-element blocks.
  */
 #include <math.h>
 #include <stdint.h>
@@ -242,7 +244,7 @@ ORC_API void orc_quantize_mxfp8_rowwise(const uint16_t* x, int64_t rows, int64_t
 }
 
 ORC_API int64_t orc_colwise_padded_cols(int32_t ngroups, int64_t rows) {
-    return 32 * ((int64_t)ngroups + (rows + 31) / 32);
+    return 128 * ((int64_t)ngroups + (rows + 127) / 128);
 }
 
 ORC_API void orc_quantize_mxfp8_colwise_t(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -256,7 +258,7 @@ ORC_API void orc_quantize_mxfp8_colwise_t(const uint16_t* x, int64_t rows, int64
         float v[32];
         for (int32_t g = 0; g < ngroups; ++g) {
             const int64_t m0 = offsets[g], m1 = offsets[g + 1];
-            const int64_t c0 = 32 * ((int64_t)g + m0 / 32);
+            const int64_t c0 = 128 * ((int64_t)g + m0 / 128);
             for (int64_t j = 0; m0 + 32 * j < m1; ++j) {
                 const int64_t mb = m0 + 32 * j;
                 const int n = (int)((m1 - mb) < 32 ? (m1 - mb) : 32);

@@ -38,9 +38,10 @@ def test_library_exports_every_declared_symbol(bsq):
 
 def test_version_and_helpers(bsq):
     assert bsq.ABI_VERSION == 2
-    assert bsq.bsq_colwise_padded_cols(32, 32768) == 32 * (32 + 1024)
-    assert bsq.bsq_colwise_padded_cols(3, 0) == 96
-    assert bsq.bsq_colwise_padded_cols(2, 33) == 32 * (2 + 2)
+    assert bsq.bsq_colwise_padded_cols(32, 32768) == 128 * (32 + 256)
+    assert bsq.bsq_colwise_padded_cols(3, 0) == 384
+    assert bsq.bsq_colwise_padded_cols(2, 129) == 128 * (2 + 2)
+    assert bsq.bsq_colwise_padded_cols(2, 33) == 128 * (2 + 1)
     assert bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_FWD, 0, 1, 64, 64) == 0
     assert bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_FWD, 32, 1, 64, 64) % 256 == 0
     assert bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_BWD, 32, 1, 64, 64) > bsq.bsq_workspace_size(

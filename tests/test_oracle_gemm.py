@@ -152,7 +152,7 @@ def test_dgrad_matches_exact_blocks(orc):
         m0, m1 = off[e], off[e + 1]
         if m0 == m1:
             continue
-        c0 = 32 * (e + woff[e] // 32)
+        c0 = 128 * (e + woff[e] // 128)
         ref, absum = _mx_exact_tn(dy_q[0][m0:m1], dy_q[1][:, m0:m1], wt_q[0][:, c0:c0 + n],
                                   wt_q[1][c0 // 32:(c0 + n) // 32, :])
         assert np.all(np.abs(dx[m0:m1] - ref) <= 1e-12 * absum + 1e-300)
@@ -174,7 +174,7 @@ def test_wgrad_matches_exact_blocks_and_outer_products(orc):
         if m0 == m1:
             assert not dw[e].any()
             continue
-        c0 = 32 * (e + m0 // 32)
+        c0 = 128 * (e + m0 // 128)
         L = 32 * ((m1 - m0 + 31) // 32)
         ref, absum = _mx_exact_tn(dyt[0][:, c0:c0 + L], dyt[1][c0 // 32:(c0 + L) // 32, :],
                                   xt[0][:, c0:c0 + L], xt[1][c0 // 32:(c0 + L) // 32, :])

@@ -235,14 +235,14 @@ def test_mxfp8_colwise_t_matches_rowwise_on_transposed_segments(orc):
     off = np.maximum.accumulate(off)
     x = make_quantize_input(rng, rows, cols)
     codes, scale = orc.quantize_mxfp8_colwise_t(x, off)
-    P = 32 * (G + (rows + 31) // 32)
+    P = 128 * (G + (rows + 127) // 128)
     assert codes.shape == (cols, P) and scale.shape == (P // 32, cols)
     covered = np.zeros(P, bool)
     for g in range(G):
         m0, m1 = int(off[g]), int(off[g + 1])
-        c0 = 32 * (g + m0 // 32)
+        c0 = 128 * (g + m0 // 128)
         L = 32 * ((m1 - m0 + 31) // 32)
-        assert c0 % 32 == 0 and not covered[c0:c0 + L].any()
+        assert c0 % 128 == 0 and not covered[c0:c0 + L].any()
         covered[c0:c0 + L] = True
         seg = np.zeros((cols, L), np.uint16)
         seg[:, :m1 - m0] = x[m0:m1].T
