@@ -224,6 +224,7 @@ def main():
     fwd_mx = fwd_mxfp8_compare(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M,
                                {k: stage_ms[k] for k in ("gemm_fwd_gate_up", "gemm_fwd_down")}, ws_f)
     bf16_base = bf16_baseline(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, stage_ms, fwd_mx, ws_f)
+    frozen = frozen_w4a16(bsq, torch, dev, x, h, q_wgu, q_wdn, off, E, Hd, I, M, bf16_base, ws_f)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -245,6 +246,7 @@ def main():
         "quantize": quant,
         "fwd_mxfp8": fwd_mx,
         "bf16_baseline": bf16_base,
+        "frozen_w4a16": frozen,
     }
     print(json.dumps(out))
 
@@ -396,6 +398,40 @@ def bf16_baseline(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, stage_ms,
         out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK["f16"], 4),
                      "speedup_nvfp4v_fwd_vs_bf16": round(ms / stage_ms[name], 3),
                      "speedup_mxfp8_fwd_vs_bf16": round(ms / fwd_mx[name]["ms"], 3)}
+    del y_gu, y_dn
+    return out
+
+
+def frozen_w4a16(bsq, torch, dev, x, h, q_wgu, q_wdn, off, E, Hd, I, M, bf16_base, ws, reps=10):
+    """Frozen experts in packed storage: the forward expert GEMMs with bf16
+    activations against the NVFP4-variant weights of the step (4.5 bits per
+    weight), dequantized to bf16 inside the kernel (bsq_grouped_gemm_w4a16),
+    outside the step; compared with the bf16 baseline on the same shapes."""
+    y_gu = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    y_dn = torch.empty((M, Hd), dtype=torch.bfloat16, device=dev)
+    wbytes = lambda q: sum(t.numel() * t.element_size() for t in q)
+    cases = {
+        "gemm_fwd_gate_up": (lambda: bsq.bsq_grouped_gemm_w4a16(x, q_wgu, off, 2 * I, Hd, y=y_gu, workspace=ws),
+                             2.0 * M * 2 * I * Hd, wbytes(q_wgu), 2 * E * 2 * I * Hd),
+        "gemm_fwd_down": (lambda: bsq.bsq_grouped_gemm_w4a16(h, q_wdn, off, Hd, I, y=y_dn, workspace=ws),
+                          2.0 * M * Hd * I, wbytes(q_wdn), 2 * E * Hd * I),
+    }
+    stream = torch.cuda.current_stream()
+    out = {"operands": "bf16 activations, NVFP4-variant packed weights dequantized to bf16 in-kernel, bf16 MFMA"}
+    for name, (fn, fl, wb, wb16) in cases.items():
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_mfma_peak": round(tf / PEAK["f16"], 4),
+                     "weight_bytes": wb, "weight_bytes_bf16": wb16, "weight_compression": round(wb16 / wb, 3),
+                     "speedup_vs_bf16": round(bf16_base[name]["ms"] / ms, 3)}
     del y_gu, y_dn
     return out
 

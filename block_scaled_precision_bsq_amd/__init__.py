@@ -45,6 +45,7 @@ _SIGS = {
                               ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_fwd_mxfp8": ([P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_bf16": ([P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
+    "bsq_grouped_gemm_w4a16": ([P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
     "bsq_workspace_size": ([INT, I32, I64, I64, I64], ctypes.c_size_t),
     "bsq_colwise_padded_cols": ([I32, I64], I64),
     "bsq_status_string": ([INT], ctypes.c_char_p),
@@ -322,6 +323,31 @@ def bsq_grouped_gemm_bf16(x, w, offsets, n, k, y_dtype=BSQ_BF16, y=None, workspa
            _lib.bsq_grouped_gemm_bf16(_ptr(x), _ptr(w), _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype,
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)))
+    return y
+
+
+def bsq_grouped_gemm_w4a16(x, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, workspace=None, stream=None):
+    """Frozen-expert GEMM: x [m_total, k] bf16 against packed weights
+    w_q = (codes [E*n, k/2], bscale [E*n, k/16], rscale [E*n]) from
+    bsq_quantize_nvfp4v, dequantized to bf16 inside the kernel."""
+    _dev(x, "x", _BF16)
+    _dev(offsets, "offsets", (torch.int32,))
+    w_codes, w_bscale, w_rscale = w_q
+    E = offsets.numel() - 1
+    m_total = x.shape[0]
+    for t, nm, shape, dt in ((x, "x", (m_total, k), None), (w_codes, "w codes", (E * n, k // 2), torch.uint8),
+                             (w_bscale, "w bscale", (E * n, k // 16), torch.uint8),
+                             (w_rscale, "w rscale", (E * n,), torch.float32)):
+        if tuple(t.shape) != shape or not t.is_contiguous() or (dt is not None and t.dtype != dt):
+            raise ValueError(f"{nm} must be contiguous with shape {shape}")
+    dev = x.device
+    if y is None:
+        y = torch.empty((m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev)
+    _check("bsq_grouped_gemm_w4a16",
+           _lib.bsq_grouped_gemm_w4a16(_ptr(x), _ptr(w_codes), _ptr(w_bscale), _ptr(w_rscale), _ptr(offsets), E,
+                                       m_total, n, k, _ptr(y), y_dtype, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
     return y
 
 

@@ -305,6 +305,30 @@ bsq_status bsq_grouped_gemm_bf16(const void* x_bf16, const void* w_bf16, const i
     return bsq::launch_gemm_bwd_mxfp8(a, persistent_grid(), stream) == hipSuccess ? BSQ_OK : BSQ_ERR_HIP;
 }
 
+bsq_status bsq_grouped_gemm_w4a16(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_bscale,
+                                  const float* w_rscale, const int32_t* offsets, int32_t num_experts,
+                                  int64_t m_total, int64_t n, int64_t k, void* y, bsq_dtype y_dtype,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_experts < 1 || m_total < 0 || n < 0 || k < 0) return BSQ_ERR_INVALID_ARG;
+    if (y_dtype != BSQ_BF16 && y_dtype != BSQ_F32) return BSQ_ERR_INVALID_ARG;
+    if (!offsets || !workspace || !w_codes || !w_bscale || !w_rscale) return BSQ_ERR_INVALID_ARG;
+    if (m_total > 0 && (!x_bf16 || !y)) return BSQ_ERR_INVALID_ARG;
+    if (num_experts > bsq::MAX_EXPERTS) return BSQ_ERR_UNSUPPORTED;
+    if (n == 0 || k == 0 || n % 64 || k % 64) return BSQ_ERR_UNSUPPORTED;
+    if (!aligned(workspace, 256) || !aligned(w_codes, 16) || !aligned(w_bscale, 4) || !aligned(w_rscale, 4) ||
+        (m_total > 0 && !aligned(x_bf16, 16)))
+        return BSQ_ERR_UNSUPPORTED;
+    if (256 * 2 * k >= kMaxBufferOffset || m_total >= (int64_t)1 << 31) return BSQ_ERR_UNSUPPORTED;
+    if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, n, k))
+        return BSQ_ERR_WORKSPACE_TOO_SMALL;
+    if (m_total == 0) return BSQ_OK;
+    // dgrad-style tiles: reduction k, output width n, B the packed rows of W_e
+    bsq::BwdArgs a{static_cast<const uint8_t*>(x_bf16), nullptr, w_codes, w_bscale, nullptr, nullptr, nullptr,
+                   nullptr, offsets, num_experts, m_total, k, n, 0, 0, y, y_dtype == BSQ_F32 ? 1 : 0, 0,
+                   static_cast<int32_t*>(workspace), 1, 0, 1, w_rscale};
+    return bsq::launch_gemm_bwd_mxfp8(a, persistent_grid(), stream) == hipSuccess ? BSQ_OK : BSQ_ERR_HIP;
+}
+
 bsq_status bsq_debug_status(const void* workspace, hipStream_t stream, int32_t* error_word_host) {
     if (!workspace || !error_word_host) return BSQ_ERR_INVALID_ARG;
     if (hipStreamSynchronize(stream) != hipSuccess) return BSQ_ERR_HIP;

@@ -30,6 +30,13 @@
 // double-buffered in registers per 64-byte k step: the MFMAs of step t run
 // while step t+1 is read from LDS, and a ring slot is refilled as soon as both
 // of its steps sit in registers.
+//
+// Two more operand modes share the tile loop (OPS): plain bf16 operands (the
+// bf16 baseline) and bf16 activations against packed NVFP4-variant weights
+// (frozen expert storage): B fragments arrive as E2M1 codes plus E4M3 block
+// scales and are dequantized to bf16 in registers -- every E2M1 x E4M3
+// product is exact in bf16 -- and the weight rows' fp32 scales are applied
+// in the epilogue.
 #include "device_common.h"
 #include "gemm_common.h"
 #include "gemm_pipe.h"
@@ -56,6 +63,7 @@ struct BwdSlot {
 };
 struct BwdSmem {
     BwdSlot slot[2];
+    float rs[256];  // packed-weight mode: fp32 scales of the tile's output columns
 };
 constexpr uint32_t SLOT_BYTES = sizeof(BwdSlot);
 static_assert(SLOT_BYTES >= 128 * 512, "a bf16 epilogue pass stages 128 rows of 512 bytes in one slot");
@@ -79,6 +87,7 @@ struct BwdFrag {
 // offsets at k = 0 (rows past the tile read as zero).
 struct BwdTile {
     i32x4 dA, dB, dAs, dBs;
+    const float* rs;  // packed-weight mode: fp32 scales of the tile's output columns
     uint32_t lda, ldb, ldas, ldbs, R;
     int rows_a, rows_b, nsteps;
     char* c;
@@ -92,6 +101,38 @@ struct BwdTile {
 // each) on the same 32 bytes per lane -- bytes [16g, +16) then [32+16g, +16),
 // i.e. elements 8g.. and 16+8g.. of the 32 the step holds, the bf16 MFMA's
 // k order for lane group g.
+// Operand modes of the tile loop.
+constexpr int OPS_MX = 0;    // MXFP8 codes and E8M0 scales on both sides
+constexpr int OPS_BF16 = 1;  // bf16 on both sides
+constexpr int OPS_W4 = 2;    // bf16 A, NVFP4-variant B dequantized in registers
+
+// Packed-weight B fragment of one k step: the lane's code dword for the
+// step's first 16 elements sits in f[0], the one for the second 16 in f[4]
+// (elements 8g.. of each half, row lr), and byte HF of s is the E4M3 scale
+// of half HF.  Half HF becomes the four bf16 dwords f[4HF .. 4HF+3] the
+// bf16 MFMA of that half takes: E2M1 pairs to fp32 (exact), times the block
+// scale in fp32 (exact: at most 6 significant bits), high halves packed (the
+// products are bf16 values, so nothing is rounded).
+template <int HF>
+__device__ __forceinline__ void w4_dequant_half(int8v& f, uint32_t s) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t w = (uint32_t)f[4 * HF];
+    const float sc = __builtin_amdgcn_cvt_f32_fp8((int)s, HF);
+    // byte q of w holds elements 2q (low nibble) and 2q + 1
+    const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    auto pk = [&](const f32x2 v) {
+        return (int)__builtin_amdgcn_perm(__float_as_uint(v[1] * sc), __float_as_uint(v[0] * sc), 0x07060302u);
+    };
+    const int o0 = pk(v0), o1 = pk(v1), o2 = pk(v2), o3 = pk(v3);
+    f[4 * HF] = o0;
+    f[4 * HF + 1] = o1;
+    f[4 * HF + 2] = o2;
+    f[4 * HF + 3] = o3;
+}
+
 template <bool BF16>
 __device__ __forceinline__ float16v mfma_step(const int8v& a, const int8v& b, int sa, int sb, float16v c) {
     if constexpr (BF16) {
@@ -108,18 +149,21 @@ __device__ __forceinline__ float16v mfma_step(const int8v& a, const int8v& b, in
     }
 }
 
-// BF16: the same tile loop over plain bf16 operands (the bf16 baseline of
-// the expert GEMM): no scales, a k step is 32 elements (64 bytes) and the
-// reduction length is counted in bytes.
-template <bool OUT_F32, bool WGRAD, bool BF16>
+// OPS_BF16 / OPS_W4: the same tile loop over bf16 A rows (a k step is 32
+// elements, 64 bytes; the reduction length is counted in A bytes), against
+// bf16 B rows or packed NVFP4-variant B rows.
+template <bool OUT_F32, bool WGRAD, int OPS>
 __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
+    constexpr bool BF16 = OPS != OPS_MX;  // bf16 A and bf16 MFMAs
+    constexpr bool W4 = OPS == OPS_W4;
     // DMA instructions per wave per super-stage: 16 code rows, the A scales
     // (four 64-byte pieces of block-major bytes for dgrad, whose token rows
     // start anywhere; one packed 256-byte block for wgrad, whose rows start
     // at a multiple of 256) and one packed 256-byte block of B scales; bf16
-    // operands carry no scales.
-    static_assert(!(BF16 && WGRAD), "the bf16 mode runs the row-ragged tiles only");
-    constexpr int SS_DMA = BF16 ? 16 : (WGRAD ? 18 : 21);
+    // operands carry no scales; packed weights take 2 code instructions (32
+    // bytes of 256 rows) and one scale instruction (4 bytes of 256 rows).
+    static_assert(!(BF16 && WGRAD), "the bf16 modes run the row-ragged tiles only");
+    constexpr int SS_DMA = W4 ? 11 : (BF16 ? 16 : (WGRAD ? 18 : 21));
     extern __shared__ __align__(16) uint8_t smem_raw[];
     __shared__ int s_tile;
 
@@ -166,6 +210,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         int64_t lda, ldas, ldb, ldbs, R, ldc;
         int rows_a, rows_b;
         char* c;
+        const float* rs = nullptr;
         if constexpr (!WGRAD) {
             // dX[m][k] = sum_n dY[m][n] Wt_e[k][n]
             const int KT = (int)((p.K + BWD_BN - 1) / BWD_BN);
@@ -176,7 +221,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             // block-major scales: block j of rows r0.. starts at base + j * rows_total + r0
             a = p.dy_codes + m0 * p.N; as = p.dy_scale + m0;
             lda = p.N; ldas = p.m_total; rows_a = (int)min((int64_t)BWD_BM, off1 - m0);
-            if constexpr (BF16) {
+            if constexpr (W4) {
+                // bf16 rows x [M][N]; expert e's packed weight rows [K] of N/2
+                // code bytes and N/16 E4M3 scale bytes
+                a = p.dy_codes + m0 * p.N * 2; as = p.dy_codes;
+                lda = 2 * p.N; ldas = 0;
+                b = p.wt_codes + ((int64_t)e * p.K + k0) * (p.N / 2);
+                bs = p.wt_scale + ((int64_t)e * p.K + k0) * (p.N / 16);
+                ldb = p.N / 2; ldbs = p.N / 16;
+            } else if constexpr (BF16) {
                 // bf16 rows: x [M][N] and expert e's weight rows [K][N], 2 bytes each
                 a = p.dy_codes + m0 * p.N * 2; as = p.dy_codes;
                 lda = 2 * p.N; ldas = 0;
@@ -193,6 +246,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             rows_b = (int)min((int64_t)BWD_BN, p.K - k0);
             R = BF16 ? 2 * p.N : p.N;  // bytes of k per row
             c = reinterpret_cast<char*>(p.out) + (m0 * p.K + k0) * esz; ldc = p.K;
+            if constexpr (W4) rs = p.wt_rscale + (int64_t)e * p.K + k0;
         } else {
             // dW_e[n][k] = sum_{m in e} dY^T[n][m] X^T[k][m]
             const int KT = (int)((p.K + BWD_BN - 1) / BWD_BN);
@@ -219,6 +273,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         ts.rows_b = __builtin_amdgcn_readfirstlane(rows_b);
         ts.nsteps = (int)((ts.R + 63) / 64);  // 64-byte MFMA k steps
         ts.c = uniform_ptr(c);
+        ts.rs = rs;
         ts.ldcb = __builtin_amdgcn_readfirstlane((uint32_t)(ldc * esz));
         // code instruction i (0..7) of this wave covers rows 64 * wave + 8i + lane / 8
         const int drow0 = 64 * wave + (lane >> 3);
@@ -244,10 +299,44 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
     // chunk or a 32-element scale block past R reads as zero.
     auto issue_part = [&](const BwdTile& ts, int S, auto PC) {
         constexpr int part = decltype(PC)::value;
-        if constexpr (BF16 && part >= 8) return;  // no scales
+        if constexpr (BF16 && !W4 && part >= 8) return;  // no scales
+        if constexpr (W4 && part >= 11 && part != 12) return;
         const int lane = lane_of() & 63;
         const uint32_t q = (uint32_t)S & 1;
         const uint32_t kbase = (uint32_t)S * SS_BK;
+        if constexpr (W4 && part >= 8) {
+            // Packed weight rows: 32 code bytes and 4 E4M3 scale bytes per row
+            // per super-stage (64 elements).  Parts 8 and 9: code instruction
+            // c = 2 * wave + part - 8 covers rows 32c + lane / 2, 16-byte half
+            // lane & 1, landing as [row][32 bytes].  Part 10: the scale dwords
+            // of rows 64 * wave + lane.  Part 12, with the tile's second
+            // super-stage only: the rows' fp32 scales into rs (read by the
+            // epilogue, after which the next tile's second super-stage is
+            // issued).
+            if constexpr (part < 10) {
+                // LDS half lane & 1 of a row holds code half (lane & 1) ^ bit 2
+                // of the row, which halves the bank conflicts of the reads
+                const int c = 2 * wave + (part - 8);
+                const int row = 32 * c + (lane >> 1);
+                const uint32_t bo = (uint32_t)S * 32u + 16u * (uint32_t)((lane & 1) ^ ((row >> 2) & 1));
+                const bool ok = (row < ts.rows_b) & (bo < ts.ldb);
+                dma16(ts.dB, ok ? (uint32_t)row * ts.ldb + bo : OOB,
+                      lds_at<offsetof(BwdSlot, b)>(lds0 + q * SLOT_BYTES + 1024u * (uint32_t)c));
+            } else if constexpr (part == 10) {
+                const int row = 64 * wave + lane;
+                const uint32_t so = (uint32_t)S * 4u;
+                const bool ok = (row < ts.rows_b) & (so < ts.ldbs);
+                dma4(ts.dBs, ok ? (uint32_t)row * ts.ldbs + so : OOB,
+                     lds_at<offsetof(BwdSlot, sb)>(lds0 + q * SLOT_BYTES + 256u * (uint32_t)wave));
+            } else {
+                if (S == 1) {
+                    const int row = 64 * wave + lane;
+                    dma4(make_desc(uniform_ptr(ts.rs)), row < ts.rows_b ? 4u * (uint32_t)row : OOB,
+                         lds_at<offsetof(BwdSmem, rs)>(lds0 + 256u * (uint32_t)wave));
+                }
+            }
+            return;
+        }
         if constexpr (part < 8) {
             constexpr int i = part;
             const int row = 64 * wave + 8 * i + (lane >> 3);
@@ -257,8 +346,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             const uint32_t base = lds0 + q * SLOT_BYTES + 8192u * (uint32_t)wave;
             dma16(ts.dA, (okk & (row < ts.rows_a)) ? ts.vra + (uint32_t)(8 * i) * ts.lda + ko : OOB,
                   lds_at<offsetof(BwdSlot, a) + 1024u * i>(base));
-            dma16(ts.dB, (okk & (row < ts.rows_b)) ? ts.vrb + (uint32_t)(8 * i) * ts.ldb + ko : OOB,
-                  lds_at<offsetof(BwdSlot, b) + 1024u * i>(base));
+            if constexpr (!W4)
+                dma16(ts.dB, (okk & (row < ts.rows_b)) ? ts.vrb + (uint32_t)(8 * i) * ts.ldb + ko : OOB,
+                      lds_at<offsetof(BwdSlot, b) + 1024u * i>(base));
         } else if constexpr (part < 12) {
             // dgrad A scales: instruction i covers k block (4 * wave + i) >> 2 of
             // the super-stage, rows 64 * ((4 * wave + i) & 3) + lane, one
@@ -332,6 +422,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         // rows of group i, part 2i+1 the B rows.
         auto read_part = [&](int t, BwdFrag& f, int part) {
             const uint32_t q = ((uint32_t)t >> 1) & 1, h = (uint32_t)t & 1;
+            if constexpr (W4) {
+                // parts 0..3: packed B fragments (two code dwords and the
+                // row's scale dword, dequantized later), parts 4..7: A
+                if (part < 4) {
+                    const uint32_t row = (uint32_t)(wn * 128 + 32 * part + lr);
+                    const uint32_t co = q * SLOT_BYTES + (uint32_t)offsetof(BwdSlot, b) + row * 32u +
+                                        16u * (h ^ ((row >> 2) & 1u)) + 4u * (uint32_t)g;
+                    f.b[part][0] = *(const __attribute__((address_space(3))) int*)(lds + co);
+                    f.b[part][4] = *(const __attribute__((address_space(3))) int*)(lds + co + 8u);
+                    f.sb[part] = (int)(*(const __attribute__((address_space(3))) uint32_t*)(
+                                           lds + q * SLOT_BYTES + (uint32_t)offsetof(BwdSlot, sb) + row * 4u) >>
+                                       (16u * h));
+                    return;
+                }
+                part = 2 * (part - 4);
+            }
             const int i = part >> 1;
             const uint32_t es = (part & 1) ? 1u : ESA;
             const uint32_t so = q * SLOT_BYTES + ((part & 1) ? fsb : fsa) + es * (h * 512u + 32u * i);
@@ -348,6 +454,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         auto read = [&](int t, BwdFrag& f) {
 #pragma unroll
             for (int part = 0; part < 8; ++part) read_part(t, f, part);
+        };
+        // packed B: half-fragment hf2 (0..7) of the fragments read by read_part
+        auto dequant = [&](BwdFrag& f, int hf2) {
+            if constexpr (W4) {
+                if (hf2 & 1)
+                    w4_dequant_half<1>(f.b[hf2 >> 1], (uint32_t)f.sb[hf2 >> 1]);
+                else
+                    w4_dequant_half<0>(f.b[hf2 >> 1], (uint32_t)f.sb[hf2 >> 1]);
+            }
         };
 
         float16v acc[4][4];
@@ -374,6 +489,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                 const int i = k >> 2, j = k & 3;
                 acc[i][j] = mfma_step<BF16>(cf.a[i], cf.b[j], cf.sa[i], cf.sb[j], acc[i][j]);
                 if (k >= 2 && k < 10) read_part(t + 1, nf, k - 2);
+                if (W4 && k >= 8) dequant(nf, k - 8);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -407,6 +523,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                     default: break;
                 }
                 if (k >= 4 && k < 12) read_part(t + 1, nf, k - 4);
+                if (W4 && k >= 8) dequant(nf, k - 8);
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
@@ -417,6 +534,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         block_barrier();
         BwdFrag X, Y;
         read(0, X);
+        if constexpr (W4) {
+            wait_lgkmcnt0();
+#pragma unroll
+            for (int hf2 = 0; hf2 < 8; ++hf2) dequant(X, hf2);
+        }
         int t = 0;
         for (; t + 1 < cur.nsteps; t += 2) {
             step_even(t, X, Y);
@@ -446,6 +568,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
             const __amdgpu_buffer_rsrc_t rc = make_rsrc(cur.c, 0x7FFFFFFFu);
             __attribute__((address_space(3))) uint8_t* st =
                 (__attribute__((address_space(3))) uint8_t*)(smem_raw) + SLOT_BYTES;
+            // packed weights: the fp32 scale of column wn*128 + 32j + lr
+            float rsj[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (W4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    rsj[j] = *(const __attribute__((address_space(3))) float*)(
+                        lds + offsetof(BwdSmem, rs) + 4u * (uint32_t)(wn * 128 + 32 * j + lr));
+            }
             if constexpr (OUT_F32) {
                 // f32: four passes of 64 rows (pass i: every wave's row group
                 // i), staged row r = wm * 32 + (row % 32) keeps 1024 bytes; its
@@ -463,7 +593,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                         for (int v = 0; v < 16; ++v) {
                             const uint32_t o = ((j & 1) ? wod : wev) + 256u * (j >> 1) +
                                                (uint32_t)(8 * (v >> 2) + (v & 3)) * 1024u;
-                            *(__attribute__((address_space(3))) float*)(st + o) = acc[pass][j][v];
+                            *(__attribute__((address_space(3))) float*)(st + o) =
+                                W4 ? acc[pass][j][v] * rsj[j] : acc[pass][j][v];
                         }
                     wait_lgkmcnt0();
                     block_barrier();
@@ -511,7 +642,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
                                 const uint32_t o = (uint32_t)P * 1024u + 512u * (uint32_t)half +
                                                    ((16u * (uint32_t)k + 4u * (uint32_t)(w & 3)) ^ sx);
                                 *(__attribute__((address_space(3))) uint32_t*)(st + o) =
-                                    pack_bf16x2(acc[2 * pass + ii][j][v], acc[2 * pass + ii][j][v + 1]);
+                                    W4 ? pack_bf16x2(acc[2 * pass + ii][j][v] * rsj[j],
+                                                     acc[2 * pass + ii][j][v + 1] * rsj[j])
+                                       : pack_bf16x2(acc[2 * pass + ii][j][v], acc[2 * pass + ii][j][v + 1]);
                             }
                     wait_lgkmcnt0();
                     block_barrier();
@@ -566,12 +699,14 @@ hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s) {
     static bool attr_set = false;  // idempotent; racing writers set the same value
     const int lds_max = (int)(sizeof(BwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E));
     if (!attr_set) {
-        const void* ks[6] = {reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, true, false>),
-                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false, false>),
-                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, true, false>),
-                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false, false>),
-                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false, true>),
-                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false, true>)};
+        const void* ks[8] = {reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, true, OPS_MX>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false, OPS_MX>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, true, OPS_MX>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false, OPS_MX>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false, OPS_BF16>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false, OPS_BF16>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<true, false, OPS_W4>),
+                             reinterpret_cast<const void*>(&k_gemm_bwd_mxfp8<false, false, OPS_W4>)};
         for (const void* k : ks) {
             err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
             if (err != hipSuccess) return err;
@@ -579,24 +714,30 @@ hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s) {
         attr_set = true;
     }
     const size_t lds = sizeof(BwdSmem) + lds_table_bytes(args.E);
-#define BSQ_GEMM_LAUNCH(F32, WG, B16) \
-    hipLaunchKernelGGL((k_gemm_bwd_mxfp8<F32, WG, B16>), dim3(grid), dim3(256), lds, s, args)
-    if (args.bf16) {
-        if (args.wgrad) return hipErrorInvalidValue;  // not a bf16 mode
-        if (args.out_f32)
-            BSQ_GEMM_LAUNCH(true, false, true);
-        else
-            BSQ_GEMM_LAUNCH(false, false, true);
+#define BSQ_GEMM_LAUNCH(F32, WG, OPS) \
+    hipLaunchKernelGGL((k_gemm_bwd_mxfp8<F32, WG, OPS>), dim3(grid), dim3(256), lds, s, args)
+    if (args.bf16 || args.w4) {
+        if (args.wgrad || (args.bf16 && args.w4)) return hipErrorInvalidValue;  // row-ragged tiles only
+        if (args.w4) {
+            if (args.out_f32)
+                BSQ_GEMM_LAUNCH(true, false, OPS_W4);
+            else
+                BSQ_GEMM_LAUNCH(false, false, OPS_W4);
+        } else if (args.out_f32) {
+            BSQ_GEMM_LAUNCH(true, false, OPS_BF16);
+        } else {
+            BSQ_GEMM_LAUNCH(false, false, OPS_BF16);
+        }
     } else if (args.out_f32) {
         if (args.wgrad)
-            BSQ_GEMM_LAUNCH(true, true, false);
+            BSQ_GEMM_LAUNCH(true, true, OPS_MX);
         else
-            BSQ_GEMM_LAUNCH(true, false, false);
+            BSQ_GEMM_LAUNCH(true, false, OPS_MX);
     } else {
         if (args.wgrad)
-            BSQ_GEMM_LAUNCH(false, true, false);
+            BSQ_GEMM_LAUNCH(false, true, OPS_MX);
         else
-            BSQ_GEMM_LAUNCH(false, false, false);
+            BSQ_GEMM_LAUNCH(false, false, OPS_MX);
     }
 #undef BSQ_GEMM_LAUNCH
     return hipGetLastError();

@@ -178,13 +178,18 @@ struct BwdArgs {
     int wgrad;   // 0: dgrad tiles, 1: wgrad tiles
     int32_t* plan;
     // dgrad tiles only: 0 = B is the COLWISE_T weight transpose Wt [K][Pw]
-    // (expert e at column e*(N+32)); 1 = B is a ROWWISE MXFP8 weight stack
+    // (expert e at column 128*(e + e*N/128)); 1 = B is a ROWWISE MXFP8 weight stack
     // W [E*K][N] with block-major scales [N/32][E*K] (the forward MXFP8 GEMM,
     // whose reduction is N here and whose output width is K).
     int b_rows;
     // 1: plain bf16 operands (the bf16 baseline), dgrad-style tiles with B as
     // a row-major weight stack (b_rows layout, 2 bytes per element, no scales)
     int bf16;
+    // 1: bf16 A rows against a packed NVFP4-variant weight stack (frozen
+    // experts): wt_codes [E*K][N/2], wt_scale [E*K][N/16] E4M3, wt_rscale
+    // [E*K] fp32; dgrad-style tiles, reduction N, output width K
+    int w4;
+    const float* wt_rscale;
 };
 
 hipError_t launch_plan(const int32_t* offsets, int E, int64_t m_total, int mode, int bm, int nt, int kt,

@@ -315,6 +315,32 @@ bsq_status bsq_grouped_gemm_bf16(const void* x_bf16, const void* w_bf16, const i
                                  int32_t num_experts, int64_t m_total, int64_t n, int64_t k, void* y,
                                  bsq_dtype y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * bsq_grouped_gemm_w4a16 -- forward expert grouped GEMM over frozen experts
+ * kept in packed form ("Scaling and Optimizing Frontier Model Training",
+ * low-precision expert quantization: frozen expert weights stored in a
+ * packed low-precision format, about 4x smaller than bf16, and dequantized to
+ * bf16 on the fly in the forward).  The pages do not name the packed format;
+ * this library takes its NVFP4 variant (4.5 bits per weight, 3.56x smaller
+ * than bf16), as written by bsq_quantize_nvfp4v for W viewed as [E*n][k]:
+ *   y[m][j] = s_w[e*n + j] * sum_k x[m][k] * (e2m1(q_w) * S_w)[e*n + j][k]
+ * for every row m of expert e's segment.  Each E2M1 x E4M3 product is exact
+ * in bf16, so the weights reach the bf16 MFMA undistorted; fp32 accumulation
+ * in a fixed order per element; the fp32 row scale s_w is applied to the
+ * fp32 sum before the output rounding.
+ *   x_bf16 [m_total][k] row-major, 16-byte aligned.
+ *   w_codes [num_experts*n][k/2] (16-byte aligned), w_bscale
+ *   [num_experts*n][k/16] E4M3, w_rscale [num_experts*n] fp32 (4-byte
+ *   aligned): the three outputs of bsq_quantize_nvfp4v.
+ *   y [m_total][n] in y_dtype.  n % 64 == 0, k % 64 == 0, num_experts >= 1;
+ *   workspace as for bsq_grouped_gemm_fwd (BSQ_OP_GEMM_FWD).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP.
+ */
+bsq_status bsq_grouped_gemm_w4a16(const void* x_bf16, const uint8_t* w_codes, const uint8_t* w_bscale,
+                                  const float* w_rscale, const int32_t* offsets, int32_t num_experts,
+                                  int64_t m_total, int64_t n, int64_t k, void* y, bsq_dtype y_dtype,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace the GEMM entry points need (host function, no GPU use).
  * op is BSQ_OP_GEMM_FWD or BSQ_OP_GEMM_BWD; returns 0 for invalid arguments. */
 size_t bsq_workspace_size(int op, int32_t num_experts, int64_t m_total, int64_t n, int64_t k);

@@ -327,6 +327,28 @@ def grouped_gemm_bf16(x_bf16, w_bf16, offsets, rows=None) -> np.ndarray:
     return y
 
 
+def grouped_gemm_w4a16(x_bf16, w_q, offsets, rows=None) -> np.ndarray:
+    """Frozen-expert forward GEMM over packed weights ("Scaling and Optimizing
+    Frontier Model Training", low-precision expert quantization: frozen
+    experts kept in a packed low-precision format and dequantized to bf16 on
+    the fly), in float64: Y[m, j] = sum_k X[m, k] * W_hat_e[j, k] for m in
+    segment e, with the bf16 activations taken exactly and W_hat the decoded
+    NVFP4-variant weights (codes, bscale, rscale) stacked as [E*N, K]."""
+    x = _bf16(x_bf16)
+    off = np.asarray(offsets, np.int64)
+    E = len(off) - 1
+    N = w_q[0].shape[0] // E
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows, np.int64)
+    exp_of = _expert_of_rows(off, rows)
+    y = np.zeros((len(rows), N), np.float64)
+    f64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for e in np.unique(exp_of):
+        sel = np.nonzero(exp_of == e)[0]
+        sl = slice(int(e) * N, (int(e) + 1) * N)
+        y[sel] = f64(x[rows[sel]]) @ dequant_nvfp4v(w_q[0][sl], w_q[1][sl], w_q[2][sl]).T
+    return y
+
+
 def grouped_gemm_dgrad(dy_q, wt_q, offsets, n, rows=None, absolute=False) -> np.ndarray:
     """dX[m, k] = sum_n dY_hat[m, n] * W_hat_e[n, k] (float64).
 

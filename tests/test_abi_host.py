@@ -97,6 +97,12 @@ def test_gemm_host_checks(bsq):
     assert b(*bargs(64, 128, 4, needb)) == bsq.BSQ_ERR_INVALID_ARG     # unknown flag
     assert b(*bargs(96, 128, 3, needb)) == bsq.BSQ_ERR_UNSUPPORTED     # n % 64
     assert b(*bargs(64, 128, 3, needb - 1)) == bsq.BSQ_ERR_WORKSPACE_TOO_SMALL
+    w = L.bsq_grouped_gemm_w4a16
+    wargs = lambda n, k, ws, rs=FAKE: (FAKE, FAKE, FAKE, rs, FAKE, 4, 64, n, k, FAKE, bsq.BSQ_BF16, FAKE, ws, None)
+    assert w(*wargs(64, 96, need)) == bsq.BSQ_ERR_UNSUPPORTED          # k % 64
+    assert w(*wargs(96, 128, need)) == bsq.BSQ_ERR_UNSUPPORTED         # n % 64
+    assert w(*wargs(64, 128, need, rs=None)) == bsq.BSQ_ERR_INVALID_ARG  # no row scales
+    assert w(*wargs(64, 128, need - 1)) == bsq.BSQ_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_product_path_has_no_oracle_or_fallback():

@@ -259,3 +259,64 @@ def test_single_expert_is_dense(orc):
     assert np.allclose(y, ref, rtol=1e-12, atol=0)
     yf = bf16_bits_to_f32(x).astype(np.float64) @ bf16_bits_to_f32(w).astype(np.float64).T
     assert np.linalg.norm(y - yf) / np.linalg.norm(yf) < 0.2
+
+
+def packed_exact_weights(rng, rows, k, jlo=-6, jhi=6):
+    """bf16 weight rows the NVFP4 variant represents exactly: block 0 of each
+    row holds a 6 * 448 = 2688 element (so A = 2688 and s_row = A / 2688 = 1)
+    and E2M1 multiples of 448 (S_0 = E4M3(448 * 2688 / 2688) = 448); every
+    other 16-block holds a +-6 * 2^j element and E2M1 multiples of 2^j
+    (S_b = E4M3(448 * 6 * 2^j / 2688) = 2^j).  Returns (bf16 bits, float64)."""
+    from workloads import f32_to_bf16_bits
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    nb = k // 16
+    s = np.ones((rows, nb)) * 448.0
+    s[:, 1:] = 2.0 ** rng.integers(jlo, jhi + 1, (rows, nb - 1))
+    v = mags[rng.integers(0, 8, (rows, k))] * np.where(rng.random((rows, k)) < 0.5, -1, 1)
+    v[:, ::16] = 6 * np.where(rng.random((rows, nb)) < 0.5, -1, 1)  # every block reaches its max
+    w = v * np.repeat(s, 16, axis=1)
+    bits = f32_to_bf16_bits(w.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32(bits).astype(np.float64), w)
+    return bits, w
+
+
+def test_w4a16_exact_on_representable_weights(orc):
+    """Frozen-expert GEMM: weights the packed format holds exactly decode to
+    themselves, and with integer activations the grouped product equals the
+    plain float64 product of the original bf16 inputs, expert by expert
+    (empty expert, one-row expert, row order given by offsets)."""
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(31)
+    counts = [7, 0, 1, 20]
+    E, n, k = len(counts), 12, 64
+    off = offsets_from_counts(counts)
+    M = int(off[-1])
+    wb, wv = packed_exact_weights(rng, E * n, k)
+    w_q = orc.quantize_nvfp4v(wb)
+    assert np.all(w_q[2] == 1.0)
+    assert np.array_equal(orc.dequant_nvfp4v(*w_q), wv)
+    xi = rng.integers(-8, 9, (M, k)).astype(np.float64)
+    y = orc.grouped_gemm_w4a16(f32_to_bf16_bits(xi.astype(np.float32)), w_q, off)
+    for e in range(E):
+        m0, m1 = int(off[e]), int(off[e + 1])
+        assert np.array_equal(y[m0:m1], xi[m0:m1] @ wv[e * n:(e + 1) * n].T)
+    sub = np.array([M - 1, 0, 8])
+    assert np.array_equal(orc.grouped_gemm_w4a16(f32_to_bf16_bits(xi.astype(np.float32)), w_q, off, rows=sub),
+                          y[sub])
+
+
+def test_w4a16_applies_row_scale_and_block_scales(orc):
+    """Against exact rationals on a tiny case with arbitrary (non power of
+    two) row and block scales: Y = sum_k x * e2m1 * S_b, times s_row."""
+    rng = np.random.default_rng(32)
+    x = normal_bf16(rng, (3, 32))
+    w = normal_bf16(rng, (4, 32), 0.02)
+    w_q = orc.quantize_nvfp4v(w)
+    y = orc.grouped_gemm_w4a16(x, w_q, np.array([0, 3], np.int32))
+    xv = bf16_bits_to_f32(x)
+    wi = nvfp4v_int(w_q[0], w_q[1])
+    for m in range(3):
+        for j in range(4):
+            exact = sum(Fraction(float(xv[m, q])) * Fraction(int(wi[j, q]), 1024) for q in range(32))
+            exact *= Fraction(float(w_q[2][j]))
+            assert abs(Fraction(y[m, j]) - exact) <= abs(exact) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 300)
