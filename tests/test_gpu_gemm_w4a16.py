@@ -107,3 +107,13 @@ def test_w4a16_full_size_sampled(orc, bsq_gpu, which):
         ref = orc.grouped_gemm_w4a16(xr, w_q, np.array([0, len(rows)], np.int32))
         got = _np(y[torch.from_numpy(rows).cuda()][:, colsd]).astype(np.float64)
         check_groups(got, ref, [((which, e), np.arange(len(rows)))])
+
+
+@pytest.mark.parametrize("E", [200, 900])
+def test_w4a16_many_experts(orc, bsq_gpu, E):
+    """Many small experts, a third of them empty: tile decode from the LDS
+    tables (200) and from the planner's arrays in global memory (900)."""
+    rng = rng_for(7, salt=E + 3)
+    counts = rng.integers(0, 24, E)
+    counts[rng.random(E) < 0.33] = 0
+    _case(orc, bsq_gpu, list(counts), 64, 128, seed=E + 5)

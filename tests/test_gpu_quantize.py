@@ -261,6 +261,23 @@ def test_mxfp8_dual_parity(orc, bsq_gpu, counts, cols):
     assert np.array_equal(ts, _np(gts))
 
 
+@pytest.mark.parametrize("G", [200, 900])
+def test_mxfp8_dual_many_groups(orc, bsq_gpu, G):
+    """More than 61 groups (the segment lookup's wave-wide search path), a
+    third of them empty, both layouts against the oracle."""
+    rng = rng_for(4, salt=G)
+    counts = rng.integers(0, 40, G)
+    counts[rng.random(G) < 0.33] = 0
+    off = offsets_from_counts(counts)
+    M = int(off[-1])
+    x = make_quantize_input(rng, M, 160)
+    (grc, grs), (gtc, gts) = bsq_gpu.bsq_quantize_mxfp8_dual(_bf16_dev(x), _to_dev(off))
+    rc, rs = orc.quantize_mxfp8_rowwise(x)
+    tc, ts = orc.quantize_mxfp8_colwise_t(x, off)
+    assert np.array_equal(rc, _np(grc)) and np.array_equal(rs, _np(grs))
+    assert np.array_equal(tc, _np(gtc)) and np.array_equal(ts, _np(gts))
+
+
 def test_mxfp8_dual_strided_full_size_sampled(orc, bsq_gpu):
     """dGU-shaped input at full size (32768 x 4096, Zipf(1.1) over 32 experts)
     read through a leading dimension wider than the row: sampled rows checked
