@@ -291,9 +291,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd_mxfp8(BwdArgs p) {
         return ts;
     };
 
-    // DMA of super-stage S of tile ts into ring slot S % 2 (24 instructions
-    // per wave), in 12 parts of 2 so they can sit between MFMAs: parts 0..7
-    // move code rows (A and B of instruction i), parts 8..11 scale blocks.
+    // DMA of super-stage S of tile ts into ring slot S % 2 (SS_DMA
+    // instructions per wave), in 13 parts so they can sit between MFMAs:
+    // parts 0..7 move code rows (A and B of instruction i), parts 8..12 the
+    // scale blocks (or, with packed weights, the B rows and scales).
     // The lane fetches logical chunk (lane & 7) ^ swz8(row) into slot
     // lane & 7; swz8(row) depends on lane / 8 and the parity of i.  A 16-byte
     // chunk or a 32-element scale block past R reads as zero.

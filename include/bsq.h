@@ -68,7 +68,9 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define BSQ_ABI_VERSION 2
+/* 3: COLWISE_T segments start on 128-column boundaries (P changed);
+ * added bsq_quantize_mxfp8_dual and bsq_grouped_gemm_w4a16. */
+#define BSQ_ABI_VERSION 3
 
 typedef enum {
     BSQ_OK = 0,

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(bsq):
 
 
 def test_version_and_helpers(bsq):
-    assert bsq.ABI_VERSION == 2
+    assert bsq.ABI_VERSION == 3
     assert bsq.bsq_colwise_padded_cols(32, 32768) == 128 * (32 + 256)
     assert bsq.bsq_colwise_padded_cols(3, 0) == 384
     assert bsq.bsq_colwise_padded_cols(2, 129) == 128 * (2 + 2)

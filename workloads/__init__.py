@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "rng_for", "f32_to_bf16_bits", "bf16_bits_to_f32", "normal_bf16",
     "zipf_counts", "offsets_from_counts", "top2_uniform_routing", "Config",
-    "CONFIGS", "make_quantize_input", "make_expert_weights", "padded_cols",
+    "CONFIGS", "make_quantize_input", "make_expert_weights",
 ]
 
 
@@ -121,13 +121,6 @@ def make_quantize_input(rng, rows, cols, outlier_frac=0.01, outlier_mult=50.0):
 
 def make_expert_weights(rng, n_experts, n, k, sigma=0.02):
     return normal_bf16(rng, (n_experts, n, k), sigma)
-
-
-def padded_cols(n_groups: int, rows: int) -> int:
-    """Column count of the transposed, per-segment padded MXFP8 layout:
-    ``32 * (n_groups + ceil(rows / 32))`` (segments start at 32-aligned
-    columns ``32 * (g + floor(offsets[g] / 32))``)."""
-    return 32 * (n_groups + (rows + 31) // 32)
 
 
 @dataclass(frozen=True)
