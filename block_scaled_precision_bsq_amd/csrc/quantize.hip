@@ -408,8 +408,10 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_colwise_t(
             const int k = max(__builtin_popcountll(__ballot(have && st <= pc)) - 1, 0);
             const int64_t stk = 128 * ((int64_t)(g0 + k) + __builtin_amdgcn_readlane(of0, k) / 128);
             const int64_t mb = __builtin_amdgcn_readlane(of0, k) + (pc - stk);
-            const int64_t end = __builtin_amdgcn_readlane(of1, k);
-            const bool ok = pc < P && mb < end;
+            // segment bounds clamped to the input's rows, so offsets that break
+            // the precondition still never read or write outside the tensors
+            const int64_t end = min((int64_t)__builtin_amdgcn_readlane(of1, k), rows);
+            const bool ok = pc < P && mb >= 0 && mb < end;
             blk_m0[b] = uniform_i64(ok ? mb : 0);
             blk_n[b] = __builtin_amdgcn_readfirstlane(ok ? (int)min((int64_t)32, end - mb) : 0);
         }

@@ -184,8 +184,11 @@ bsq_status bsq_debug_quantize_nvfp4v_fastdiv(const void* x_bf16, int64_t rows, i
  *   x_bf16 [rows][ld_x] bf16, 16-byte aligned, ld_x % 8 == 0, ld_x >= cols.
  *   BSQ_ROWWISE: cols % 32 == 0; codes [rows][cols], scale [cols/32][rows];
  *     offsets may be NULL.
- *   BSQ_COLWISE_T: cols % 8 == 0; offsets required (num_groups >= 1);
- *     codes [cols][P], scale [P/32][cols], P = bsq_colwise_padded_cols(
+ *   BSQ_COLWISE_T: cols % 8 == 0; offsets required (num_groups >= 1),
+ *     device int32 [num_groups + 1] with 0 = offsets[0] <= ... <=
+ *     offsets[num_groups] = rows; offsets breaking this give unspecified
+ *     bytes but no access outside the buffers (segments are clamped to the
+ *     rows).  codes [cols][P], scale [P/32][cols], P = bsq_colwise_padded_cols(
  *     num_groups, rows); every output byte is written (padding = 0).
  *     Quantizing expert weights W [E][N][K] as rows = E*N with offsets
  *     {0, N, 2N, ...} gives the dgrad operand Wt: codes [K][P_w].

@@ -331,3 +331,4 @@ def test_mxfp8_gather_full_size_sampled(orc, bsq_gpu):
     ref = orc.quantize_mxfp8_rowwise(x[idx[rows]])
     assert np.array_equal(_np(codes)[rows], ref[0])
     assert np.array_equal(_np(scale)[:, rows], ref[1])
+
