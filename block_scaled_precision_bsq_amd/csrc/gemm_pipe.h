@@ -61,27 +61,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 16 bytes per lane from desc+voff to LDS lds_base + 16 * lane.  lds_base
-// is wave-uniform (it must reach M0 through an SGPR).
-__device__ __forceinline__ void dma16(i32x4 desc, uint32_t voff, uint32_t lds_base) {
+// Buffer-to-LDS DMA through the compiler's builtin, which owns M0: each lane
+// moves SIZE bytes from desc+voff to LDS, lane i's data at lds_base + 16 i
+// for SIZE 16 and at lds_base + 4 i for SIZE 4 and 1 (a byte lands
+// zero-extended in its dword).  lds_base is wave-uniform; an offset past the
+// descriptor's range reads as zero.
+template <int SIZE>
+__device__ __forceinline__ void dma_lds(i32x4 desc, uint32_t voff, uint32_t lds_base) {
     lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
+    const uint64_t base = (uint64_t)(uint32_t)desc.x | ((uint64_t)((uint32_t)desc.y & 0xFFFFu) << 32);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, desc.z, desc.w);
+    __attribute__((address_space(3))) void* dst = (__attribute__((address_space(3))) void*)(uintptr_t)lds_base;
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
+    else if constexpr (SIZE == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 1, voff, 0, 0, 0);
 }
-
-// 4 bytes per lane to lds_base + 4 * lane.
-__device__ __forceinline__ void dma4(i32x4 desc, uint32_t voff, uint32_t lds_base) {
-    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
-}
-
-// 1 byte per lane, zero-extended into the dword at lds_base + 4 * lane.
-__device__ __forceinline__ void dma1(i32x4 desc, uint32_t voff, uint32_t lds_base) {
-    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_ubyte %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(desc), "s"(lds_base) : "memory", "m0");
-}
+__device__ __forceinline__ void dma16(i32x4 desc, uint32_t voff, uint32_t lds_base) { dma_lds<16>(desc, voff, lds_base); }
+__device__ __forceinline__ void dma4(i32x4 desc, uint32_t voff, uint32_t lds_base) { dma_lds<4>(desc, voff, lds_base); }
+__device__ __forceinline__ void dma1(i32x4 desc, uint32_t voff, uint32_t lds_base) { dma_lds<1>(desc, voff, lds_base); }
 
 // LDS target base + OFF with the base laundered through an empty asm: the
 // compiler then adds OFF right at the DMA instead of hoisting one live SGPR
