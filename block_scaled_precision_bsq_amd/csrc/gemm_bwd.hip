@@ -647,6 +647,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_ws(BwdArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
     const bool dwave = wave >= 4;
     const int dw = wave & 3;
+    // When both waves of a SIMD are ready to issue an MFMA, the DMA wave's
+    // goes first, so it returns sooner to its next DMA instruction.
+    if (dwave) __builtin_amdgcn_s_setprio(1);
     const int wm = wave & 1, wn = wave >> 1;
     const int xcd = blockIdx.x & 7;
     constexpr int esz = OUT_F32 ? 4 : 2;
