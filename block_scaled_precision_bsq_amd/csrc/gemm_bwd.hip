@@ -89,12 +89,7 @@ struct BwdTile {
     uint32_t vsa[4];  // dgrad A scale rows (one byte per lane)
 };
 
-// One 64-byte k step of fragments for output block (i, j): a single
-// block-scaled fp8 MFMA (64 k), or for bf16 operands two bf16 MFMAs (16 k
-// each) on the same 32 bytes per lane -- bytes [16g, +16) then [32+16g, +16),
-// i.e. elements 8g.. and 16+8g.. of the 32 the step holds, the bf16 MFMA's
-// k order for lane group g.
-// Operand modes of the tile loops.
+// Operand modes of the tile loop.
 constexpr int OPS_MX = 0;    // MXFP8 codes and E8M0 scales on both sides
 constexpr int OPS_BF16 = 1;  // bf16 on both sides
 constexpr int OPS_W4 = 2;    // bf16 A, NVFP4-variant B dequantized in registers
@@ -126,6 +121,11 @@ __device__ __forceinline__ void w4_dequant_half(int8v& f, uint32_t s) {
     f[4 * HF + 3] = o3;
 }
 
+// One 64-byte k step of fragments for output block (i, j): a single
+// block-scaled fp8 MFMA (64 k), or for bf16 operands two bf16 MFMAs (16 k
+// each) on the same 32 bytes per lane -- bytes [16g, +16) then [32+16g, +16),
+// i.e. elements 8g.. and 16+8g.. of the 32 the step holds, the bf16 MFMA's
+// k order for lane group g.
 template <bool BF16>
 __device__ __forceinline__ float16v mfma_step(const int8v& a, const int8v& b, int sa, int sb, float16v c) {
     if constexpr (BF16) {
@@ -144,7 +144,9 @@ __device__ __forceinline__ float16v mfma_step(const int8v& a, const int8v& b, in
 
 // Number of DMA instructions in issue part `part` of a DMA wave, and of LDS
 // reads after MFMA m of a k step (refill order: B 0 after MFMA 3, A m - 4
-// after MFMA m >= 4, B 1 after MFMA 7; three reads per fragment).
+// after MFMA m >= 4, B 1 after MFMA 7; two 16-byte reads per fragment plus
+// a scale read with MXFP8 operands, three 4-byte reads per packed weight
+// fragment).
 template <bool WGRAD, int OPS>
 constexpr int ws_part_dma(int part) {
     return OPS == OPS_W4     ? (part < 11 ? 1 : 0)
@@ -162,6 +164,14 @@ __device__ __forceinline__ void ws_sched_step() {
     if constexpr (ND > 0) __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);
 }
 
+// The tile loop: 8 waves (two per SIMD), each owning a 128 x 64 block of the
+// 256 x 256 tile (4 x 2 MFMA tiles, 128 accumulators).  Waves 4..7 also issue
+// every DMA instruction, so a DMA issue that stalls on the CU's full memory
+// queue holds up only the matrix-core work of its own wave; waves 0..3 never
+// enter that queue.  Two super-stages are in flight: the refill of a ring
+// slot starts as soon as every wave holds the slot's data in registers
+// (barrier X), and the wait for the next super-stage (barrier Y) comes after
+// the first refill instructions.
 template <bool OUT_F32, bool WGRAD, int OPS>
 __global__ __launch_bounds__(512, 1) void k_gemm_bwd_ws(BwdArgs p) {
     constexpr bool BF16 = OPS != OPS_MX;  // bf16 A rows and bf16 MFMAs
