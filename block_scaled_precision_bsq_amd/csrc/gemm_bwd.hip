@@ -142,11 +142,12 @@ __device__ __forceinline__ float16v mfma_step(const int8v& a, const int8v& b, in
     }
 }
 
-// Number of DMA instructions in issue part `part` of a DMA wave, and of LDS
-// reads after MFMA m of a k step (refill order: B 0 after MFMA 3, A m - 4
-// after MFMA m >= 4, B 1 after MFMA 7; two 16-byte reads per fragment plus
-// a scale read with MXFP8 operands, three 4-byte reads per packed weight
-// fragment).
+// Number of DMA instructions in issue part `part` of a DMA wave's refills
+// (super-stages 2 onwards; part 12 of packed weights loads only with the
+// tile's second super-stage), and of LDS reads after MFMA m of a k step
+// (refill order: B 0 after MFMA 3, A m - 4 after MFMA m >= 4, B 1 after
+// MFMA 7; two 16-byte reads per fragment plus a scale read with MXFP8
+// operands, three 4-byte reads per packed weight fragment).
 template <bool WGRAD, int OPS>
 constexpr int ws_part_dma(int part) {
     return OPS == OPS_W4     ? (part < 11 ? 1 : 0)
@@ -567,7 +568,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_ws(BwdArgs p) {
             }
             if (t < cur.nsteps) {
                 wait_lgkmcnt0();
-                dq(1, 0);  // packed weights: B fragment 1 of the last step
+                // packed weights: B fragment 1 of the last step (the entry
+                // points take k % 64 == 0 for the bf16 modes, so their step
+                // count is even and this tail runs for MXFP8 operands only)
+                dq(1, 0);
                 dq(1, 1);
 #pragma unroll
                 for (int m = 0; m < 8; ++m) mm(m);
