@@ -67,14 +67,15 @@ __device__ __forceinline__ float rcp_approx(float b) {
 // row's codes cr[cols/2], block scales br[nb] and row scale *rs.
 // Scale byte of a 16-element block with |x| maximum amax_b (bf16 bits) in a
 // row with |x| maximum A > 0: S_b = E4M3_RNE(RN32(448 * a_b / A)).  The
-// numerator and denominator are exact; for a_b > 2^119 both are scaled by
-// 2^-8 to keep 448*a_b finite.
+// numerator and denominator are exact; for a_b > 2^119, where 448*a_b could
+// overflow, both are scaled by 2^-9 (0.875*a_b and A*2^-9: exact, finite,
+// same quotient).
 template <bool FASTDIV>
 __device__ __forceinline__ uint32_t nvfp4v_block_scale(uint32_t amax_b, float A) {
     const float ab = __uint_as_float(amax_b << 16);
     float num, den;
-    if (ab <= 0x1p119f) { num = 448.0f * ab; den = A; }
-    else                { num = 1.75f * ab;  den = A * 0x1p-8f; }
+    if (ab <= 0x1p119f) { num = 448.0f * ab;  den = A; }
+    else                { num = 0.875f * ab;  den = A * 0x1p-9f; }
     const float t = FASTDIV ? num * rcp_approx(den) : num / den;  // in [0, 448]
     return e4m3x4(t, 0.0f, 0.0f, 0.0f) & 0xFFu;
 }
@@ -548,10 +549,15 @@ __global__ void k_debug_e4m3(const float* __restrict__ in, uint8_t* __restrict__
 
 // ---------------------------------------------------------------- launchers
 
+// A dispatch counts its work-items in 32 bits: at most 2^24 - 1 workgroups of
+// 256 threads.
+constexpr int64_t kMaxWorkgroups = ((int64_t)1 << 24) - 1;
+
 template <bool SWIGLU, bool FASTDIV = false>
 static hipError_t launch_nvfp4v(const uint16_t* x, int64_t rows, int cols, int64_t ldx, uint8_t* codes,
                                 uint8_t* bscale, float* rscale, uint16_t* h, int64_t ldh, hipStream_t s) {
     const int nb = cols / 16;
+    if ((rows + 3) / 4 > kMaxWorkgroups) return hipErrorInvalidValue;  // beyond the host-checked sizes
     const dim3 grid((unsigned)((rows + 3) / 4));
 #define BSQ_NVFP4V_LAUNCH(BPL)                                                                       \
     hipLaunchKernelGGL((k_quantize_nvfp4v<BPL, SWIGLU, FASTDIV>), grid, dim3(256), 0, s, x, rows, cols, \
@@ -593,7 +599,7 @@ static hipError_t launch_mxfp8_rowwise(const uint16_t* x, int64_t rows, int cols
                                        uint8_t* scale, const int32_t* row_index, int64_t src_rows, hipStream_t s) {
     const int nbt = (cols / 32 + MXR_BLK - 1) / MXR_BLK;
     const int64_t nwg = ((rows + MXR_ROWS - 1) / MXR_ROWS) * nbt;
-    if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (nwg >= kMaxWorkgroups) return hipErrorInvalidValue;
     const bool a16 = (rows % 16 == 0) && ((reinterpret_cast<uintptr_t>(scale) & 15) == 0);
     if (a16)
         hipLaunchKernelGGL((k_quantize_mxfp8_rowwise<true, GATHER>), dim3((unsigned)nwg), dim3(256), 0, s, x, rows,
@@ -619,7 +625,7 @@ hipError_t launch_quantize_mxfp8_colwise_t(const uint16_t* x, int64_t rows, int 
                                            const int32_t* offsets, int ngroups, int64_t P, uint8_t* codes,
                                            uint8_t* scale, hipStream_t s) {
     const int64_t nwg = (int64_t)((cols + COLT_CH - 1) / COLT_CH) * ((P + COLT_TOK - 1) / COLT_TOK);
-    if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // beyond the host-checked sizes
+    if (nwg >= kMaxWorkgroups) return hipErrorInvalidValue;  // beyond the host-checked sizes
     const dim3 grid((unsigned)nwg);
     hipLaunchKernelGGL(k_quantize_mxfp8_colwise_t<false>, grid, dim3(256), 0, s, x, rows, cols, ldx, offsets,
                        ngroups, P, codes, scale, nullptr, nullptr);
@@ -630,7 +636,7 @@ hipError_t launch_quantize_mxfp8_dual(const uint16_t* x, int64_t rows, int cols,
                                       int ngroups, int64_t P, uint8_t* t_codes, uint8_t* t_scale, uint8_t* r_codes,
                                       uint8_t* r_scale, hipStream_t s) {
     const int64_t nwg = (int64_t)((cols + COLT_CH - 1) / COLT_CH) * ((P + COLT_TOK - 1) / COLT_TOK);
-    if (nwg >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (nwg >= kMaxWorkgroups) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nwg);
     hipLaunchKernelGGL(k_quantize_mxfp8_colwise_t<true>, grid, dim3(256), 0, s, x, rows, cols, ldx, offsets,
                        ngroups, P, t_codes, t_scale, r_codes, r_scale);
@@ -638,6 +644,7 @@ hipError_t launch_quantize_mxfp8_dual(const uint16_t* x, int64_t rows, int cols,
 }
 
 hipError_t launch_debug_encode(int which, const float* in, uint8_t* out, int64_t n, hipStream_t s) {
+    if ((n + 255) / 256 > kMaxWorkgroups) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((n + 255) / 256));
     if (which == 0)
         hipLaunchKernelGGL(k_debug_e2m1, grid, dim3(256), 0, s, in, out, n);

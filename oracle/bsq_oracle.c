@@ -138,13 +138,15 @@ ORC_API void orc_e4m3_encode_array(const float* v, uint8_t* out, int64_t n) {
 
 /* --------------------------------------------------------- NVFP4 variant */
 
-/* RN32(448 * a / A) for 0 <= a <= A, A > 0.  Both operands of the single
- * division are exact: 448*a has at most 11 significant bits, and when it could
- * overflow (a > 2^119) numerator and denominator are both scaled by 2^-8. */
+/* RN32(448 * a / A) for 0 <= a <= A, A > 0: one division of two exact
+ * operands.  448*a has at most 11 significant bits.  For a > 2^119 it could
+ * overflow, so numerator and denominator are both scaled by 2^-9 (exact: both
+ * stay above 2^110, far from the subnormal range, and 448 * 2^-9 * a < a
+ * stays finite), which leaves the exact quotient unchanged. */
 static float block_ratio(float a, float A) {
     float num, den;
-    if (a <= 0x1p119f) { num = 448.0f * a; den = A; }
-    else               { num = 1.75f * a;  den = A * 0x1p-8f; }
+    if (a <= 0x1p119f) { num = 448.0f * a;  den = A; }
+    else               { num = 0.875f * a;  den = A * 0x1p-9f; }
     return num / den;
 }
 

@@ -119,6 +119,16 @@ def test_nvfp4v_parity_edge_values(orc, bsq_gpu):
     x[9, ::16] = bf16(np.full(16, 1.0))          # one nonzero per block
     x[9, 1::16] = bf16(np.full(16, 2.0 ** -12))
     x[10] = bf16(rng.integers(-6, 7, 256) * 0.5)
+    # block maxima in [FLT_MAX / 1.75, bf16 max] = [1.94e38, 3.39e38]: the
+    # branch where 448 * a_b would overflow binary32
+    top = rng.uniform(1.95e38, 3.38e38, 16)
+    x[11] = bf16(np.repeat(top, 16) * rng.uniform(-1, 1, 256))
+    x[11, ::16] = bf16(top)
+    x[12] = bf16(np.tile([1.75 * 2.0 ** 127, 1.25 * 2.0 ** 127], 128) * np.repeat([1, -1], 128))
+    for r in range(13, 24):
+        xf = bf16_bits_to_f32(x[r]).astype(np.float64)
+        xf = xf if not np.abs(xf).max() else xf * 2.0 ** (127 - np.floor(np.log2(np.abs(xf).max())))
+        x[r] = bf16(xf)
     _nvfp4v_check(orc, bsq_gpu, x)
 
 

@@ -53,6 +53,59 @@ def test_nvfp4v_worked_row_transforms(orc):
     assert np.array_equal(c2, c0 ^ 0x88)
 
 
+def _pow2_value(tok):
+    """'m*2^e' -> float (exact), '0' -> 0.0."""
+    if "*2^" not in tok:
+        return float(tok)
+    m, e = tok.split("*2^")
+    return math.ldexp(float(m), int(e))
+
+
+def _golden_huge():
+    d = {}
+    for ln in golden_lines("nvfp4v_huge_row.txt"):
+        k, v = ln.split(":", 1)
+        d[k] = v.split()
+    return d
+
+
+def test_nvfp4v_huge_row(orc):
+    """Block maxima above FLT_MAX / 1.75 (the branch where 448 * a_b would
+    overflow): the hand-worked bytes, scale bytes 7e 7a, not 7e 7e."""
+    g = _golden_huge()
+    xf = np.array([[_pow2_value(t) for t in g["x"]]], np.float64)
+    x = bf16(xf)
+    assert np.array_equal(bf16_bits_to_f32(x).astype(np.float64), xf)  # every value bf16-exact
+    codes, bscale, rscale = orc.quantize_nvfp4v(x)
+    assert bscale[0].tolist() == [int(b, 16) for b in g["bscale"]]
+    assert rscale.view(np.uint32)[0] == int(g["rscale_bits"][0], 16)
+    assert _unpack(codes)[0].tolist() == [int(c, 16) for c in g["codes"]]
+    assert codes[0].tolist() == [int(b, 16) for b in g["packed"]]
+    # the same row times 2^-100 takes the unscaled branch and gives the same bytes
+    c1, b1, r1 = orc.quantize_nvfp4v(bf16(xf * 2.0 ** -100))
+    assert np.array_equal(c1, codes) and np.array_equal(b1, bscale)
+    assert r1.view(np.uint32)[0] == int(g["rscale_bits_scaled"][0], 16)
+
+
+def test_nvfp4v_power_of_two_equivariance_to_top_of_range(orc):
+    """Each row scaled by the power of two that puts its max in [2^127, 2^128)
+    (most rows then hold a block maximum above FLT_MAX / 1.75): the bytes of
+    every row are unchanged and s_row scales exactly, whichever side of the
+    2^119 switch its block maxima fall on."""
+    rng = np.random.default_rng(17)
+    xf = bf16_bits_to_f32(make_quantize_input(rng, 48, 256)).astype(np.float64)
+    xf[5, 16:] *= 2.0 ** -12          # rows whose block maxima straddle 2^119 after scaling
+    xf[6, ::16] *= 0.7
+    p = 127 - np.floor(np.log2(np.abs(xf).max(axis=1)))
+    big = xf * np.exp2(p)[:, None]
+    assert np.all(np.abs(big).max(axis=1) >= 2.0 ** 127) and np.all(np.isfinite(big))
+    assert np.mean(np.abs(big).max(axis=1) > np.finfo(np.float32).max / 1.75) > 0.3
+    c0, b0, r0 = orc.quantize_nvfp4v(bf16(xf))
+    c1, b1, r1 = orc.quantize_nvfp4v(bf16(big))
+    assert np.array_equal(c0, c1) and np.array_equal(b0, b1)
+    assert np.array_equal(r1.astype(np.float64), r0.astype(np.float64) * np.exp2(p))
+
+
 def test_nvfp4v_zero_row_and_zero_block(orc):
     x = np.zeros((2, 64), np.float32)
     x[1, 16:32] = np.linspace(-3, 3, 16)
