@@ -78,6 +78,16 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _empty(stream, shape, dtype, device):
+    """torch.empty on the caching allocator's pool of ``stream`` when one is
+    given: a block freed here (the workspace) or later (an output) is then
+    reused only in ``stream``'s order, never while its kernels still run."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -118,9 +128,9 @@ def bsq_quantize_nvfp4v(x, codes=None, bscale=None, rscale=None, offsets=None, s
     _dev(x, "x", _BF16)
     rows, cols, ld = _rows_ld(x)
     dev = x.device
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if codes is None else codes
-    bscale = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev) if bscale is None else bscale
-    rscale = torch.empty((rows,), dtype=torch.float32, device=dev) if rscale is None else rscale
+    codes = _empty(stream, (rows, cols // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    bscale = _empty(stream, (rows, cols // 16), dtype=torch.uint8, device=dev) if bscale is None else bscale
+    rscale = _empty(stream, (rows,), dtype=torch.float32, device=dev) if rscale is None else rscale
     for t, nm, shape in ((codes, "codes", (rows, cols // 2)), (bscale, "bscale", (rows, cols // 16)),
                          (rscale, "rscale", (rows,))):
         if tuple(t.shape) != shape or not t.is_contiguous():
@@ -138,9 +148,9 @@ def bsq_debug_quantize_nvfp4v_fastdiv(x, stream=None):
     _dev(x, "x", _BF16)
     rows, cols, ld = _rows_ld(x)
     dev = x.device
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
-    bscale = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
-    rscale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    codes = _empty(stream, (rows, cols // 2), dtype=torch.uint8, device=dev)
+    bscale = _empty(stream, (rows, cols // 16), dtype=torch.uint8, device=dev)
+    rscale = _empty(stream, (rows,), dtype=torch.float32, device=dev)
     _check("bsq_debug_quantize_nvfp4v_fastdiv",
            _lib.bsq_debug_quantize_nvfp4v_fastdiv(_ptr(x), rows, cols, ld, _ptr(codes), _ptr(bscale), _ptr(rscale),
                                                   _stream(stream)))
@@ -156,8 +166,8 @@ def bsq_quantize_mxfp8_gather(x, row_index, codes=None, scale=None, stream=None)
     src_rows, cols, ld = _rows_ld(x)
     rows = row_index.numel()
     dev = x.device
-    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev) if codes is None else codes
-    scale = torch.empty((cols // 32, rows), dtype=torch.uint8, device=dev) if scale is None else scale
+    codes = _empty(stream, (rows, cols), dtype=torch.uint8, device=dev) if codes is None else codes
+    scale = _empty(stream, (cols // 32, rows), dtype=torch.uint8, device=dev) if scale is None else scale
     for t, nm, shape in ((codes, "codes", (rows, cols)), (scale, "scale", (cols // 32, rows))):
         if tuple(t.shape) != shape or not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous with shape {shape}")
@@ -179,15 +189,15 @@ def bsq_swiglu_quantize_nvfp4v(gu, h=None, write_h=True, codes=None, bscale=None
     inter = cols2 // 2
     dev = gu.device
     if write_h and h is None:
-        h = torch.empty((rows, inter), dtype=torch.bfloat16, device=dev)
+        h = _empty(stream, (rows, inter), dtype=torch.bfloat16, device=dev)
     if h is not None:
         _dev(h, "h", _BF16)
         if tuple(h.shape) != (rows, inter) or (rows > 1 and h.stride(1) != 1):
             raise ValueError(f"h must be row-major with shape {(rows, inter)}")
     ldh = 0 if h is None else (h.stride(0) if rows > 1 else inter)
-    codes = torch.empty((rows, inter // 2), dtype=torch.uint8, device=dev) if codes is None else codes
-    bscale = torch.empty((rows, inter // 16), dtype=torch.uint8, device=dev) if bscale is None else bscale
-    rscale = torch.empty((rows,), dtype=torch.float32, device=dev) if rscale is None else rscale
+    codes = _empty(stream, (rows, inter // 2), dtype=torch.uint8, device=dev) if codes is None else codes
+    bscale = _empty(stream, (rows, inter // 16), dtype=torch.uint8, device=dev) if bscale is None else bscale
+    rscale = _empty(stream, (rows,), dtype=torch.float32, device=dev) if rscale is None else rscale
     for t, nm, shape in ((codes, "codes", (rows, inter // 2)), (bscale, "bscale", (rows, inter // 16)),
                          (rscale, "rscale", (rows,))):
         if tuple(t.shape) != shape or not t.is_contiguous():
@@ -215,8 +225,8 @@ def bsq_quantize_mxfp8(x, axis=BSQ_ROWWISE, offsets=None, codes=None, scale=None
         ng = offsets.numel() - 1
         Pc = bsq_colwise_padded_cols(ng, rows)
         shapes = ((cols, Pc), (Pc // 32, cols))
-    codes = torch.empty(shapes[0], dtype=torch.uint8, device=dev) if codes is None else codes
-    scale = torch.empty(shapes[1], dtype=torch.uint8, device=dev) if scale is None else scale
+    codes = _empty(stream, shapes[0], dtype=torch.uint8, device=dev) if codes is None else codes
+    scale = _empty(stream, shapes[1], dtype=torch.uint8, device=dev) if scale is None else scale
     for t, nm, shape in ((codes, "codes", shapes[0]), (scale, "scale", shapes[1])):
         if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous with shape {shape}")
@@ -242,7 +252,7 @@ def bsq_quantize_mxfp8_dual(x, offsets, row=None, t=None, stream=None):
     outs = []
     for buf, nm, shape in ((rc, "row codes", shapes[0]), (rs, "row scale", shapes[1]),
                            (tc, "t codes", shapes[2]), (ts, "t scale", shapes[3])):
-        buf = torch.empty(shape, dtype=torch.uint8, device=dev) if buf is None else buf
+        buf = _empty(stream, shape, dtype=torch.uint8, device=dev) if buf is None else buf
         if tuple(buf.shape) != tuple(shape) or not buf.is_contiguous():
             raise ValueError(f"{nm} must be contiguous with shape {shape}")
         outs.append(buf)
@@ -252,10 +262,10 @@ def bsq_quantize_mxfp8_dual(x, offsets, row=None, t=None, stream=None):
     return (outs[0], outs[1]), (outs[2], outs[3])
 
 
-def _workspace(op, E, m_total, n, k, workspace, dev):
+def _workspace(op, E, m_total, n, k, workspace, dev, stream=None):
     need = bsq_workspace_size(op, E, m_total, n, k)
     if workspace is None:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+        workspace = _empty(stream, (need,), dtype=torch.uint8, device=dev)
     if workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must hold {need} bytes")
     return workspace
@@ -273,8 +283,8 @@ def bsq_grouped_gemm_fwd(a_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, work
         raise ValueError("weights must hold num_experts * n rows")
     dev = a_codes.device
     if y is None:
-        y = torch.empty((m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
-    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev)
+        y = _empty(stream, (m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev, stream)
     _check("bsq_grouped_gemm_fwd",
            _lib.bsq_grouped_gemm_fwd(_ptr(a_codes), _ptr(a_bscale), _ptr(a_rscale), _ptr(w_codes), _ptr(w_bscale),
                                      _ptr(w_rscale), _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype,
@@ -296,8 +306,8 @@ def bsq_grouped_gemm_fwd_mxfp8(x_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None
         raise ValueError("weights must hold num_experts * n rows")
     dev = x_codes.device
     if y is None:
-        y = torch.empty((m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
-    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev)
+        y = _empty(stream, (m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev, stream)
     _check("bsq_grouped_gemm_fwd_mxfp8",
            _lib.bsq_grouped_gemm_fwd_mxfp8(_ptr(x_codes), _ptr(x_scale), _ptr(w_codes), _ptr(w_scale),
                                            _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype, _ptr(workspace),
@@ -317,8 +327,8 @@ def bsq_grouped_gemm_bf16(x, w, offsets, n, k, y_dtype=BSQ_BF16, y=None, workspa
             raise ValueError(f"{nm} must be contiguous with shape {shape}")
     dev = x.device
     if y is None:
-        y = torch.empty((m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
-    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev)
+        y = _empty(stream, (m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev, stream)
     _check("bsq_grouped_gemm_bf16",
            _lib.bsq_grouped_gemm_bf16(_ptr(x), _ptr(w), _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype,
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -342,8 +352,8 @@ def bsq_grouped_gemm_w4a16(x, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, work
             raise ValueError(f"{nm} must be contiguous with shape {shape}")
     dev = x.device
     if y is None:
-        y = torch.empty((m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
-    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev)
+        y = _empty(stream, (m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, n, k, workspace, dev, stream)
     _check("bsq_grouped_gemm_w4a16",
            _lib.bsq_grouped_gemm_w4a16(_ptr(x), _ptr(w_codes), _ptr(w_bscale), _ptr(w_rscale), _ptr(offsets), E,
                                        m_total, n, k, _ptr(y), y_dtype, _ptr(workspace),
@@ -361,10 +371,10 @@ def bsq_grouped_gemm_bwd(offsets, m_total, n, k, dy_q=None, wt_q=None, dyt_q=Non
     E = offsets.numel() - 1
     dev = offsets.device
     if flags & BSQ_DGRAD and dx is None and m_total > 0:
-        dx = torch.empty((m_total, k), dtype=torch.float32 if dx_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+        dx = _empty(stream, (m_total, k), dtype=torch.float32 if dx_dtype == BSQ_F32 else torch.bfloat16, device=dev)
     if flags & BSQ_WGRAD and dw is None:
-        dw = torch.empty((E, n, k), dtype=torch.float32 if dw_dtype == BSQ_F32 else torch.bfloat16, device=dev)
-    workspace = _workspace(BSQ_OP_GEMM_BWD, E, m_total, n, k, workspace, dev)
+        dw = _empty(stream, (E, n, k), dtype=torch.float32 if dw_dtype == BSQ_F32 else torch.bfloat16, device=dev)
+    workspace = _workspace(BSQ_OP_GEMM_BWD, E, m_total, n, k, workspace, dev, stream)
     dy_q = dy_q or (None, None)
     wt_q = wt_q or (None, None)
     dyt_q = dyt_q or (None, None)
@@ -385,13 +395,13 @@ def bsq_debug_status(workspace, stream=None):
 
 def bsq_debug_encode_e2m1(x, out=None, stream=None):
     _dev(x, "x", (torch.float32,))
-    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    out = _empty(stream, x.shape, dtype=torch.uint8, device=x.device) if out is None else out
     _check("bsq_debug_encode_e2m1", _lib.bsq_debug_encode_e2m1(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
     return out
 
 
 def bsq_debug_encode_e4m3(x, out=None, stream=None):
     _dev(x, "x", (torch.float32,))
-    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    out = _empty(stream, x.shape, dtype=torch.uint8, device=x.device) if out is None else out
     _check("bsq_debug_encode_e4m3", _lib.bsq_debug_encode_e4m3(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
     return out

@@ -29,6 +29,11 @@ hipError_t launch_debug_encode(int, const float*, uint8_t*, int64_t, hipStream_t
 namespace {
 
 constexpr int64_t kMaxBufferOffset = (int64_t)1 << 31;  // 32-bit buffer offsets
+// A dispatch counts its work-items in 32 bits (workgroups x 256 threads <
+// 2^32).  Row quantizers run one wave per row, four rows per workgroup of 256
+// threads; the debug encoders one element per thread.
+constexpr int64_t kMaxNvfp4vRows = ((int64_t)1 << 26) - 4;
+constexpr int64_t kMaxDebugElems = ((int64_t)1 << 32) - 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -92,7 +97,7 @@ bsq_status bsq_quantize_nvfp4v(const void* x_bf16, int64_t rows, int64_t cols, i
     if (!x_bf16 || !codes || !bscale || !rscale || ld_x < cols) return BSQ_ERR_INVALID_ARG;
     if (cols % 16 || cols > 16384 || ld_x % 8 || !aligned(x_bf16, 16) || !aligned(codes, 8) || !aligned(rscale, 4))
         return BSQ_ERR_UNSUPPORTED;
-    if (rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
+    if (rows > kMaxNvfp4vRows) return BSQ_ERR_UNSUPPORTED;
     return from_hip(bsq::launch_quantize_nvfp4v(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x, codes,
                                                 bscale, rscale, stream));
 }
@@ -104,7 +109,7 @@ bsq_status bsq_debug_quantize_nvfp4v_fastdiv(const void* x_bf16, int64_t rows, i
     if (!x_bf16 || !codes || !bscale || !rscale || ld_x < cols) return BSQ_ERR_INVALID_ARG;
     if (cols % 16 || cols > 16384 || ld_x % 8 || !aligned(x_bf16, 16) || !aligned(codes, 8) || !aligned(rscale, 4))
         return BSQ_ERR_UNSUPPORTED;
-    if (rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
+    if (rows > kMaxNvfp4vRows) return BSQ_ERR_UNSUPPORTED;
     return from_hip(bsq::launch_quantize_nvfp4v_fastdiv(static_cast<const uint16_t*>(x_bf16), rows, (int)cols, ld_x,
                                                         codes, bscale, rscale, stream));
 }
@@ -133,7 +138,7 @@ bsq_status bsq_swiglu_quantize_nvfp4v(const void* gu_bf16, int64_t rows, int64_t
         !aligned(rscale, 4))
         return BSQ_ERR_UNSUPPORTED;
     if (h_bf16 && (ld_h % 8 || !aligned(h_bf16, 16))) return BSQ_ERR_UNSUPPORTED;
-    if (rows > ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
+    if (rows > kMaxNvfp4vRows) return BSQ_ERR_UNSUPPORTED;
     return from_hip(bsq::launch_swiglu_quantize_nvfp4v(static_cast<const uint16_t*>(gu_bf16), rows, (int)inter, ld_gu,
                                                        static_cast<uint16_t*>(h_bf16), ld_h, codes, bscale, rscale,
                                                        stream));
@@ -236,6 +241,10 @@ bsq_status bsq_grouped_gemm_bwd(const uint8_t* dy_codes, const uint8_t* dy_scale
         m_total >= (int64_t)1 << 31 || (n / 32 + 1) * (m_total + 256) >= kMaxBufferOffset ||
         (P / 32 + 1) * (n + k) >= kMaxBufferOffset || (Pw / 32 + 1) * k >= kMaxBufferOffset)
         return BSQ_ERR_UNSUPPORTED;
+    // per-tile output offsets are 32-bit: 256 rows of k outputs (dx and dw)
+    if ((dg && 256 * k * (dx_dtype == BSQ_F32 ? 4 : 2) >= kMaxBufferOffset) ||
+        (wg && 256 * k * (dw_dtype == BSQ_F32 ? 4 : 2) >= kMaxBufferOffset))
+        return BSQ_ERR_UNSUPPORTED;
     if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_BWD, num_experts, m_total, n, k))
         return BSQ_ERR_WORKSPACE_TOO_SMALL;
     int32_t* plan0 = static_cast<int32_t*>(workspace);
@@ -273,6 +282,8 @@ bsq_status bsq_grouped_gemm_fwd_mxfp8(const uint8_t* x_codes, const uint8_t* x_s
     if (256 * k >= kMaxBufferOffset || m_total >= (int64_t)1 << 31 ||
         (k / 32 + 1) * (m_total + 256) >= kMaxBufferOffset || (k / 32 + 1) * (wrows + 256) >= kMaxBufferOffset)
         return BSQ_ERR_UNSUPPORTED;
+    // per-tile output offsets are 32-bit: 256 rows of n outputs
+    if (256 * n * (y_dtype == BSQ_F32 ? 4 : 2) >= kMaxBufferOffset) return BSQ_ERR_UNSUPPORTED;
     if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, n, k))
         return BSQ_ERR_WORKSPACE_TOO_SMALL;
     if (m_total == 0) return BSQ_OK;
@@ -296,6 +307,8 @@ bsq_status bsq_grouped_gemm_bf16(const void* x_bf16, const void* w_bf16, const i
     if (!aligned(workspace, 256) || !aligned(w_bf16, 16) || (m_total > 0 && !aligned(x_bf16, 16)))
         return BSQ_ERR_UNSUPPORTED;
     if (256 * 2 * k >= kMaxBufferOffset || m_total >= (int64_t)1 << 31) return BSQ_ERR_UNSUPPORTED;
+    // per-tile output offsets are 32-bit: 256 rows of n outputs
+    if (256 * n * (y_dtype == BSQ_F32 ? 4 : 2) >= kMaxBufferOffset) return BSQ_ERR_UNSUPPORTED;
     if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, n, k))
         return BSQ_ERR_WORKSPACE_TOO_SMALL;
     if (m_total == 0) return BSQ_OK;
@@ -319,6 +332,8 @@ bsq_status bsq_grouped_gemm_w4a16(const void* x_bf16, const uint8_t* w_codes, co
         (m_total > 0 && !aligned(x_bf16, 16)))
         return BSQ_ERR_UNSUPPORTED;
     if (256 * 2 * k >= kMaxBufferOffset || m_total >= (int64_t)1 << 31) return BSQ_ERR_UNSUPPORTED;
+    // per-tile output offsets are 32-bit: 256 rows of n outputs
+    if (256 * n * (y_dtype == BSQ_F32 ? 4 : 2) >= kMaxBufferOffset) return BSQ_ERR_UNSUPPORTED;
     if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, n, k))
         return BSQ_ERR_WORKSPACE_TOO_SMALL;
     if (m_total == 0) return BSQ_OK;
@@ -344,7 +359,7 @@ bsq_status bsq_debug_encode_e2m1(const float* in, uint8_t* out, int64_t n, hipSt
     if (n < 0) return BSQ_ERR_INVALID_ARG;
     if (n == 0) return BSQ_OK;
     if (!in || !out) return BSQ_ERR_INVALID_ARG;
-    if (n >= ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
+    if (n > kMaxDebugElems) return BSQ_ERR_UNSUPPORTED;
     return from_hip(bsq::launch_debug_encode(0, in, out, n, stream));
 }
 
@@ -352,7 +367,7 @@ bsq_status bsq_debug_encode_e4m3(const float* in, uint8_t* out, int64_t n, hipSt
     if (n < 0) return BSQ_ERR_INVALID_ARG;
     if (n == 0) return BSQ_OK;
     if (!in || !out) return BSQ_ERR_INVALID_ARG;
-    if (n >= ((int64_t)1 << 40)) return BSQ_ERR_UNSUPPORTED;
+    if (n > kMaxDebugElems) return BSQ_ERR_UNSUPPORTED;
     return from_hip(bsq::launch_debug_encode(1, in, out, n, stream));
 }
 
