@@ -41,6 +41,7 @@ _SIGS = {
     "bsq_quantize_mxfp8": ([P, I64, I64, I64, INT, P, I32, P, P, P], INT),
     "bsq_quantize_mxfp8_dual": ([P, I64, I64, I64, P, I32, P, P, P, P, P], INT),
     "bsq_grouped_gemm_fwd": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
+    "bsq_grouped_gemm_fwd_noalloc": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P], INT),
     "bsq_grouped_gemm_bwd": ([P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, INT, ctypes.c_uint, P,
                               ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_fwd_mxfp8": ([P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
@@ -290,6 +291,27 @@ def bsq_grouped_gemm_fwd(a_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, work
                                      _ptr(w_rscale), _ptr(offsets), E, m_total, n, k, _ptr(y), y_dtype,
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+    return y
+
+
+def bsq_grouped_gemm_fwd_noalloc(a_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, stream=None):
+    """bsq_grouped_gemm_fwd with the planner workspace inside the library (no
+    workspace argument; the library allocates nothing).  ``y`` is allocated
+    here only when not given."""
+    a_codes, a_bscale, a_rscale = a_q
+    w_codes, w_bscale, w_rscale = w_q
+    _dev(offsets, "offsets", (torch.int32,))
+    E = offsets.numel() - 1
+    m_total = a_codes.shape[0]
+    if w_codes.shape[0] != E * n:
+        raise ValueError("weights must hold num_experts * n rows")
+    if y is None:
+        y = _empty(stream, (m_total, n), dtype=torch.float32 if y_dtype == BSQ_F32 else torch.bfloat16,
+                   device=a_codes.device)
+    _check("bsq_grouped_gemm_fwd_noalloc",
+           _lib.bsq_grouped_gemm_fwd_noalloc(_ptr(a_codes), _ptr(a_bscale), _ptr(a_rscale), _ptr(w_codes),
+                                             _ptr(w_bscale), _ptr(w_rscale), _ptr(offsets), E, m_total, n, k, _ptr(y),
+                                             y_dtype, _stream(stream)))
     return y
 
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsq.so")
 
-SOURCES = ["quantize.hip", "plan.hip", "gemm_fwd.hip", "gemm_bwd.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "plan.hip", "gemm_fwd.hip", "gemm_bwd.hip", "abi.cpp", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -69,8 +69,9 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 
 /* 3: COLWISE_T segments start on 128-column boundaries (P changed);
- * added bsq_quantize_mxfp8_dual and bsq_grouped_gemm_w4a16. */
-#define BSQ_ABI_VERSION 3
+ * added bsq_quantize_mxfp8_dual and bsq_grouped_gemm_w4a16.
+ * 4: added bsq_grouped_gemm_fwd_noalloc. */
+#define BSQ_ABI_VERSION 4
 
 typedef enum {
     BSQ_OK = 0,
@@ -244,6 +245,25 @@ bsq_status bsq_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_bscale,
                                 const int32_t* offsets, int32_t num_experts, int64_t m_total, int64_t n,
                                 int64_t k, void* y, bsq_dtype y_dtype, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * bsq_grouped_gemm_fwd_noalloc -- bsq_grouped_gemm_fwd without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * operands, outputs, results (bit for bit) and errors as bsq_grouped_gemm_fwd;
+ * the planner tables and claim counters live in a device array inside the
+ * library, one per GPU, sized for num_experts <= 4096 (33,280 bytes, held
+ * until the process ends).  Allocates nothing: no hipMalloc, no allocating
+ * library call.  Every call on one GPU uses that GPU's single array, so calls
+ * that may overlap on one GPU (other streams, other host threads) race and
+ * must be serialized by the caller; each call's planner rewrites every word
+ * its GEMM reads, so no clearing is needed between calls.
+ * Errors: as bsq_grouped_gemm_fwd, plus UNSUPPORTED for num_experts > 4096.
+ */
+bsq_status bsq_grouped_gemm_fwd_noalloc(const uint8_t* a_codes, const uint8_t* a_bscale, const float* a_rscale,
+                                        const uint8_t* w_codes, const uint8_t* w_bscale, const float* w_rscale,
+                                        const int32_t* offsets, int32_t num_experts, int64_t m_total, int64_t n,
+                                        int64_t k, void* y, bsq_dtype y_dtype, hipStream_t stream);
 
 /*
  * bsq_grouped_gemm_bwd -- backward expert grouped GEMMs in MXFP8

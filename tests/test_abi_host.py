@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(bsq):
 
 
 def test_version_and_helpers(bsq):
-    assert bsq.ABI_VERSION == 3
+    assert bsq.ABI_VERSION == 4
     assert bsq.bsq_colwise_padded_cols(32, 32768) == 128 * (32 + 256)
     assert bsq.bsq_colwise_padded_cols(3, 0) == 384
     assert bsq.bsq_colwise_padded_cols(2, 129) == 128 * (2 + 2)
@@ -112,3 +112,13 @@ def test_product_path_has_no_oracle_or_fallback():
         if fn.endswith(".py"):
             src = open(os.path.join(pkg, fn)).read()
             assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_noalloc_host_checks(bsq):
+    """The allocation-free forward GEMM rejects expert counts its device array
+    cannot plan for, before touching the device."""
+    f = bsq._lib.bsq_grouped_gemm_fwd_noalloc
+    args = lambda E: (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, E, 64, 64, 128, FAKE, bsq.BSQ_BF16, None)
+    assert f(*args(4097)) == bsq.BSQ_ERR_UNSUPPORTED
+    assert f(*args(0)) == bsq.BSQ_ERR_INVALID_ARG
+    assert f(*args(-3)) == bsq.BSQ_ERR_INVALID_ARG
