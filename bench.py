@@ -64,48 +64,37 @@ def copy_mode():
                       "ms_per_copy": round(ms, 4), "gbps": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is built and measured "
-              f"for a single MI355X", file=sys.stderr)
-        sys.exit(2)
-    if args.mode == "copy":
-        copy_mode()
-        return
+def build_step(bsq, torch, dev, cfg, counts, seed):
+    """Device inputs, preallocated outputs and the stage list of one step of
+    the expert shard ``cfg`` (routed token counts ``counts``): the forward of
+    the NVFP4-variant path and the MXFP8 backward of both projections.  The
+    step allocates nothing."""
     import numpy as np
-    import torch
+    from workloads import offsets_from_counts
 
-    if not os.path.exists(os.path.join(ROOT, "block_scaled_precision_bsq_amd", "libbsq.so")):
-        from __graft_entry__ import build
-        build()
-    import block_scaled_precision_bsq_amd as bsq
-    from workloads import CONFIGS, moe_counts, offsets_from_counts
-
-    cfg = CONFIGS[3]
     E, Hd, I, M = cfg.n_experts, cfg.hidden, cfg.inter, cfg.m_total
-    counts = moe_counts(cfg)
     off_np = offsets_from_counts(counts)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    gen = torch.Generator(device=dev).manual_seed(20250)
+    gen = torch.Generator(device=dev).manual_seed(seed)
     bf = torch.bfloat16
 
     def randn(shape, sigma=1.0):
         return (torch.randn(shape, generator=gen, device=dev) * sigma).to(bf)
 
-    x = randn((M, Hd))
-    w_gu = randn((E * 2 * I, Hd), 0.02)       # [E][2I][H]: gate rows then up rows
-    w_dn = randn((E * Hd, I), 0.02)           # [E][H][I]
-    dy = randn((M, Hd), 1e-3)
-    dgu = randn((M, 2 * I), 1e-3)
+    t = {}
+    t["x"] = randn((M, Hd))
+    t["w_gu"] = randn((E * 2 * I, Hd), 0.02)       # [E][2I][H]: gate rows then up rows
+    t["w_dn"] = randn((E * Hd, I), 0.02)           # [E][H][I]
+    t["dy"] = randn((M, Hd), 1e-3)
+    t["dgu"] = randn((M, 2 * I), 1e-3)
     off = torch.from_numpy(off_np).to(dev)
+    t["off"] = off
     woff_gu = torch.arange(E + 1, dtype=torch.int32, device=dev) * (2 * I)
     woff_dn = torch.arange(E + 1, dtype=torch.int32, device=dev) * Hd
-    ws_f = torch.empty(bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_FWD, E, M, 8192, 8192), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_BWD, E, M, 8192, 8192), dtype=torch.uint8, device=dev)
+    t["ws_f"] = ws_f = torch.empty(bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_FWD, E, M, 8192, 8192), dtype=torch.uint8,
+                                   device=dev)
+    t["ws_b"] = ws_b = torch.empty(bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_BWD, E, M, 8192, 8192), dtype=torch.uint8,
+                                   device=dev)
 
-    # preallocated outputs (the step allocates nothing)
     def nv(rows, cols):
         return (torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev),
                 torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev),
@@ -120,9 +109,11 @@ def main():
         return (torch.empty((cols, P), dtype=torch.uint8, device=dev),
                 torch.empty((P // 32, cols), dtype=torch.uint8, device=dev))  # block-major scales
 
-    q_wgu, q_wdn, q_x, q_h = nv(E * 2 * I, Hd), nv(E * Hd, I), nv(M, Hd), nv(M, I)
-    gu = torch.empty((M, 2 * I), dtype=bf, device=dev)
-    h = torch.empty((M, I), dtype=bf, device=dev)
+    x, w_gu, w_dn, dy, dgu = t["x"], t["w_gu"], t["w_dn"], t["dy"], t["dgu"]
+    t["q_wgu"], t["q_wdn"], t["q_x"], t["q_h"] = q_wgu, q_wdn, q_x, q_h = (nv(E * 2 * I, Hd), nv(E * Hd, I), nv(M, Hd),
+                                                                          nv(M, I))
+    t["gu"] = gu = torch.empty((M, 2 * I), dtype=bf, device=dev)
+    t["h"] = h = torch.empty((M, I), dtype=bf, device=dev)
     y = torch.empty((M, Hd), dtype=bf, device=dev)
     q_dy, q_dgu = mxr(M, Hd), mxr(M, 2 * I)
     t_wdn, t_wgu = mxc(E * Hd, I, E), mxc(E * 2 * I, Hd, E)
@@ -131,8 +122,9 @@ def main():
     dx = torch.empty((M, Hd), dtype=bf, device=dev)
     dw_dn = torch.empty((E, Hd, I), dtype=bf, device=dev)
     dw_gu = torch.empty((E, 2 * I, Hd), dtype=bf, device=dev)
+    t["keep"] = (y, q_dy, q_dgu, t_wdn, t_wgu, t_dy, t_h, t_dgu, t_x, dh, dx, dw_dn, dw_gu)
 
-    R, C = bsq.BSQ_ROWWISE, bsq.BSQ_COLWISE_T
+    C = bsq.BSQ_COLWISE_T
     stages = [
         ("quant_nvfp4v_weights", lambda: (bsq.bsq_quantize_nvfp4v(w_gu, *q_wgu), bsq.bsq_quantize_nvfp4v(w_dn, *q_wdn))),
         ("quant_nvfp4v_x", lambda: bsq.bsq_quantize_nvfp4v(x, *q_x)),
@@ -158,7 +150,6 @@ def main():
         ("gemm_bwd_wgrad_gate_up", lambda: bsq.bsq_grouped_gemm_bwd(off, M, 2 * I, Hd, dyt_q=t_dgu, xt_q=t_x,
                                                                     flags=bsq.BSQ_WGRAD, dw=dw_gu, workspace=ws_b)),
     ]
-
     flops = {
         "gemm_fwd_gate_up": 2.0 * M * 2 * I * Hd, "gemm_fwd_down": 2.0 * M * Hd * I,
         "gemm_bwd_dgrad_down": 2.0 * M * Hd * I, "gemm_bwd_wgrad_down": 2.0 * M * Hd * I,
@@ -172,7 +163,15 @@ def main():
         "swiglu_quant_nvfp4v_h": 2 * M * 2 * I + nvb(M, I), "quant_mxfp8_dual": mxd(M, Hd) + mxd(M, 2 * I),
         "quant_mxfp8_colwise_t": mxb(E * Hd, I) + mxb(E * 2 * I, Hd) + mxb(M, I) + mxb(M, Hd),
     }
+    return t, stages, flops, qbytes
 
+
+def time_step(torch, stages, steps, warmup):
+    """Wall time per step over exactly ``steps`` steps (nothing else in the
+    timed region), then a second, instrumented pass with HIP events around
+    every stage on the launch stream.  Returns (ms per step, ms per step of
+    the instrumented pass, median ms per stage)."""
+    import numpy as np
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -183,30 +182,29 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # the timed region: exactly K steps, nothing else on the stream
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    # per-stage breakdown from a second, instrumented pass of K steps (HIP
-    # events around every stage on the launch stream)
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
-          for _ in range(args.steps)]
+          for _ in range(steps)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(ev[s])
     torch.cuda.synchronize()
-    ms_step_instr = (time.perf_counter() - t1) * 1e3 / args.steps
-    stage_ms = {nm: float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+    ms_instr = (time.perf_counter() - t1) * 1e3 / steps
+    stage_ms = {nm: float(np.median([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
                 for i, (nm, _) in enumerate(stages)}
-    total_flops = sum(flops.values())
-    breakdown = {}
+    return ms_step, ms_instr, stage_ms
+
+
+def breakdown_of(stage_ms, flops, qbytes):
+    out = {}
     for nm, ms in stage_ms.items():
         d = {"ms": round(ms, 4)}
         if nm in flops:
@@ -217,7 +215,38 @@ def main():
         if nm in qbytes:
             gbs = qbytes[nm] / (ms * 1e-3) / 1e9
             d.update({"gbps": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_GBS, 4)})
-        breakdown[nm] = d
+        out[nm] = d
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is built and measured "
+              f"for a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy":
+        copy_mode()
+        return
+    import numpy as np
+    import torch
+
+    if not os.path.exists(os.path.join(ROOT, "block_scaled_precision_bsq_amd", "libbsq.so")):
+        from __graft_entry__ import build
+        build()
+    import block_scaled_precision_bsq_amd as bsq
+    from workloads import CONFIGS, moe_counts, offsets_from_counts
+
+    cfg = CONFIGS[3]
+    E, Hd, I, M = cfg.n_experts, cfg.hidden, cfg.inter, cfg.m_total
+    counts = moe_counts(cfg)
+    off_np = offsets_from_counts(counts)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t, stages, flops, qbytes = build_step(bsq, torch, dev, cfg, counts, 20250)
+    ms_step, ms_step_instr, stage_ms = time_step(torch, stages, args.steps, args.warmup)
+    total_flops = sum(flops.values())
+    breakdown = breakdown_of(stage_ms, flops, qbytes)
     dom = max(flops, key=lambda k: stage_ms[k])
     dom_tf = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
     dom_peak = PEAK["f16"] if "fwd" in dom else PEAK["fp8"]
@@ -229,10 +258,14 @@ def main():
                 "unit": "TFLOP/s", "frac": round(dom_tf / dom_peak, 4), "traffic": traffic.get(dom)}
 
     quant = quantize_config2(bsq, torch, dev)
+    x, w_gu, w_dn, h, off, ws_f = t["x"], t["w_gu"], t["w_dn"], t["h"], t["off"], t["ws_f"]
     fwd_mx = fwd_mxfp8_compare(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M,
                                {k: stage_ms[k] for k in ("gemm_fwd_gate_up", "gemm_fwd_down")}, ws_f)
     bf16_base = bf16_baseline(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, stage_ms, fwd_mx, ws_f)
-    frozen = frozen_w4a16(bsq, torch, dev, x, h, q_wgu, q_wdn, off, E, Hd, I, M, bf16_base, ws_f)
+    frozen = frozen_w4a16(bsq, torch, dev, x, h, t["q_wgu"], t["q_wdn"], off, E, Hd, I, M, bf16_base, ws_f)
+    del t, stages, x, w_gu, w_dn, h, off, ws_f
+    torch.cuda.empty_cache()
+    cfg5 = config5_line(bsq, torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -251,13 +284,43 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown": breakdown,
+        "stage_times": "median over the K steps of HIP events around each stage on the launch stream",
         "ms_per_step_instrumented": round(ms_step_instr, 4),
         "quantize": quant,
+        "config5": cfg5,
         "fwd_mxfp8": fwd_mx,
         "bf16_baseline": bf16_base,
         "frozen_w4a16": frozen,
     }
     print(json.dumps(out))
+
+
+def config5_line(bsq, torch, dev, steps=10, warmup=3):
+    """The large, imbalanced shard: 48 experts (one GPU's share of a
+    384-expert MoE), 8 of them empty, Zipf(1.5) over the other 40, 65536
+    token-slots, hidden 7168, intermediate 2048; the same step as the
+    headline workload (every quantization and the six grouped GEMMs)."""
+    from workloads import CONFIGS, moe_counts
+    cfg = CONFIGS[5]
+    counts = moe_counts(cfg)
+    t, stages, flops, qbytes = build_step(bsq, torch, dev, cfg, counts, 50505)
+    ms_step, _, stage_ms = time_step(torch, stages, steps, warmup)
+    fwd = sum(v for k, v in flops.items() if "fwd" in k)
+    bwd = sum(v for k, v in flops.items() if "bwd" in k)
+    fwd_ms = sum(stage_ms[k] for k in flops if "fwd" in k)
+    bwd_ms = sum(stage_ms[k] for k in flops if "bwd" in k)
+    out = {"workload": "48 experts (8 empty), Zipf(1.5) over 40, 65536 token-slots, hidden 7168, intermediate 2048",
+           "max_tokens_per_expert": int(max(counts)), "min_nonempty": int(min(c for c in counts if c > 0)),
+           "steps": steps, "ms_per_step": round(ms_step, 4),
+           "gemm_tflops_per_step": round(sum(flops.values()) / (ms_step * 1e-3) / 1e12, 1),
+           "fwd_gemm_tflop": round(fwd / 1e12, 3), "fwd_gemm_ms": round(fwd_ms, 4),
+           "fwd_gemm_tflops": round(fwd / (fwd_ms * 1e-3) / 1e12, 1),
+           "bwd_gemm_tflop": round(bwd / 1e12, 3), "bwd_gemm_ms": round(bwd_ms, 4),
+           "bwd_gemm_tflops": round(bwd / (bwd_ms * 1e-3) / 1e12, 1),
+           "breakdown": breakdown_of(stage_ms, flops, qbytes)}
+    del t, stages
+    torch.cuda.empty_cache()
+    return out
 
 
 def quantize_config2(bsq, torch, dev, reps=20):
@@ -287,17 +350,29 @@ def quantize_config2(bsq, torch, dev, reps=20):
                        2 * R * C + R * C + R * C // 32 + C * P + C * P // 32),
     }
     stream = torch.cuda.current_stream()
-    out = {"workload": "quantize: 16384 x 7168 bf16 N(0,1), 72 outlier channels x50"}
-    for name, (fn, nbytes) in cases.items():
+    # 512 MB written before every timed launch: more than the 256 MB Infinity
+    # Cache, so no launch reads its input (235 MB) from the previous one's cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = {"workload": "quantize: 16384 x 7168 bf16 N(0,1), 72 outlier channels x50",
+           "timing": f"median of {reps} launches, each after a 512 MB write that evicts the 256 MB Infinity Cache; "
+                     "HIP events on the launch stream around the launch alone"}
+
+    def timed(fn):
         for _ in range(3):
             fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
+        ts = []
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps):
+            flush.fill_(i & 255)
+            ev[i][0].record(stream)
             fn()
-        b.record(stream)
+            ev[i][1].record(stream)
         torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / reps
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        return ts[len(ts) // 2]
+
+    for name, (fn, nbytes) in cases.items():
+        us = timed(fn)
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 2), "bytes": nbytes, "gbps": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_GBS, 4)}
     # Dispatch-style quantize: 4096 tokens of the same data, top-8 routing into
@@ -308,15 +383,7 @@ def quantize_config2(bsq, torch, dev, reps=20):
     gc = torch.empty((T * k, C), dtype=torch.uint8, device=dev)
     gs = torch.empty((C // 32, T * k), dtype=torch.uint8, device=dev)
     xs = x[:T]
-    for _ in range(3):
-        bsq.bsq_quantize_mxfp8_gather(xs, idx, codes=gc, scale=gs)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        bsq.bsq_quantize_mxfp8_gather(xs, idx, codes=gc, scale=gs)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / reps
+    us = timed(lambda: bsq.bsq_quantize_mxfp8_gather(xs, idx, codes=gc, scale=gs))
     nbytes = 2 * T * k * C + T * k * C + T * k * C // 32   # gathered bf16 rows read + codes + scales
     nmin = 2 * T * C + T * k * C + T * k * C // 32         # each source row once + codes + scales
     out["mxfp8_gather_dispatch"] = {"workload": "4096 tokens x 7168, top-8 into 32768 expert-sorted slots",
@@ -327,13 +394,7 @@ def quantize_config2(bsq, torch, dev, reps=20):
     # divides; how many decisions it changes against IEEE division, and its time.
     bsq.bsq_quantize_nvfp4v(x, *nv)
     fc, fb, fr = bsq.bsq_debug_quantize_nvfp4v_fastdiv(x)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        bsq.bsq_debug_quantize_nvfp4v_fastdiv(x)
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / reps
+    us = timed(lambda: bsq.bsq_debug_quantize_nvfp4v_fastdiv(x))
     nib = lambda c: torch.stack([c & 15, c >> 4], -1)
     out["nvfp4v_fastdiv_ablation"] = {
         "us": round(us, 2), "speedup_vs_ieee": round(out["nvfp4v"]["us"] / us, 3),
@@ -481,13 +542,60 @@ def measured_traffic():
     return out
 
 
+def host_cpu():
+    """CPU model and core counts of the host, read at run time."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": usable, "os_cpu_count": os.cpu_count()}
+
+
+def cpu_quantize_rates(oracle, threads):
+    """The oracle's quantizers on a bounded sample of the quantize-only
+    workload (rows of 7168 bf16 ~N(0,1) with 72 outlier channels x50):
+    algorithmic GB/s on ``threads`` threads and on one thread."""
+    from workloads import make_quantize_input, rng_for
+    C = 7168
+    x = make_quantize_input(rng_for(2, salt=91), 2048, C)
+    cases = {"nvfp4v": (oracle.quantize_nvfp4v, lambda r: 2 * r * C + r * C // 2 + r * C // 16 + 4 * r),
+             "mxfp8_rowwise": (oracle.quantize_mxfp8_rowwise, lambda r: 2 * r * C + r * C + r * C // 32)}
+    out = {"sample": f"2048 x {C} rows (all threads) and 256 x {C} rows (one thread) of the 16384 x {C} "
+                     "quantize-only workload; best of 3"}
+    for name, (fn, nbytes) in cases.items():
+        d = {}
+        for nthr, rows in ((threads, 2048), (1, 256)):
+            oracle.set_num_threads(nthr)
+            xs = x[:rows]
+            best = float("inf")
+            for _ in range(3):
+                t0 = time.perf_counter()
+                fn(xs)
+                best = min(best, time.perf_counter() - t0)
+            d["gbps_all_threads" if nthr == threads else "gbps_one_thread"] = round(nbytes(rows) / best / 1e9, 4)
+        d["threads"] = threads
+        out[name] = d
+    oracle.set_num_threads(threads)
+    return out
+
+
 def cpu_baseline(cfg, counts, off_np):
     """The oracle as it stands, on a bounded sample of the same step: for one
     expert at a time, largest first, every quantization and all six GEMMs of
     the step (forward gate/up, SwiGLU, forward down, dgrad and wgrad of both
     projections) on that expert's rows, until about ``budget_s`` seconds of
     oracle time are spent.  Rate = the GEMM flops of the experts done / the
-    oracle time (quantization included, input generation not)."""
+    oracle time (quantization included, input generation not).  Also the
+    oracle's quantizers alone, on all threads and on one."""
     import numpy as np
 
     import oracle
@@ -497,6 +605,8 @@ def cpu_baseline(cfg, counts, off_np):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = os.cpu_count() or 1
+    host = host_cpu()
+    omp_threads = oracle.max_threads()
     rng = rng_for(3, salt=55)
     Hd, I = cfg.hidden, cfg.inter
     budget_s = 20.0  # the sample stops after the first expert that ends past this
@@ -531,11 +641,15 @@ def cpu_baseline(cfg, counts, off_np):
         done.append(m)
         if t_all >= budget_s:
             break
-    return {"value": round(flops / t_all / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+    quant = cpu_quantize_rates(oracle, omp_threads)
+    return {"value": round(flops / t_all / 1e12, 5), "unit": "TFLOP/s", "cores": int(max(blas_threads, omp_threads)),
+            "kind": "oracle",
             "sample": f"the whole step (NVFP4-variant and MXFP8 quantizations, SwiGLU, float64 forward, dgrad and "
                       f"wgrad GEMMs of both projections) for the {len(done)} largest of {len(counts)} experts "
                       f"({sum(done)} of {int(np.sum(counts))} token-slots); stops after ~{budget_s:.0f} s; "
-                      f"seconds={t_all:.1f}"}
+                      f"seconds={t_all:.1f}",
+            "threads": {"blas_float64_gemm": int(blas_threads), "openmp_quantizers": int(omp_threads)},
+            **host, "quantize": quant}
 
 
 if __name__ == "__main__":

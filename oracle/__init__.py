@@ -68,6 +68,8 @@ def lib():
         L.orc_quantize_mxfp8_colwise_t.argtypes = [P, I64, I64, I64, P, I32, P, P]
         L.orc_quantize_mxfp8_colwise_t.restype = None
         L.orc_dequant_mxfp8.argtypes = [P, P, I64, I64, I64, I64, I64, P]; L.orc_dequant_mxfp8.restype = None
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]; L.orc_set_num_threads.restype = None
+        L.orc_max_threads.argtypes = []; L.orc_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -81,6 +83,16 @@ def _bf16(x) -> np.ndarray:
     if x.dtype != np.uint16:
         raise TypeError("oracle inputs are bf16 bit patterns (uint16)")
     return x
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the C oracle's parallel loops (timing only; results do not
+    depend on it)."""
+    lib().orc_set_num_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 # ------------------------------------------------------------------ codecs

@@ -50,10 +50,18 @@
  *           only the element format and the 32-element blocks.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
 #define ORC_API __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------ threading */
+
+/* Thread count of the parallel loops below (timing only: every loop writes
+ * disjoint outputs, so results do not depend on it). */
+ORC_API void orc_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+ORC_API int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- decoding */
 
