@@ -4,8 +4,9 @@ One step = the whole hot path over one batch of the 32-expert shard
 (hidden 7168, intermediate 2048, 32768 routed token-slots, Zipf(1.1) expert
 popularity), inputs resident in HBM:
   forward  : NVFP4-variant quantize of W_gu, W_down (once per weight version,
-             i.e. every optimizer step) and of X; gate/up grouped GEMM;
-             SwiGLU (harness activation) fused with the quantization of H; down grouped GEMM;
+             i.e. every optimizer step) and of X; gate/up grouped GEMM with
+             the SwiGLU harness activation in its epilogue (writes H only);
+             NVFP4-variant quantize of H; down grouped GEMM;
   backward : MXFP8 quantize of dY (row-wise and per-expert transposed), of the
              weights (transposed) and of H, dGU, X (transposed); dgrad and
              wgrad grouped GEMMs of the down and the gate/up projections.
@@ -128,10 +129,10 @@ def build_step(bsq, torch, dev, cfg, counts, seed):
     stages = [
         ("quant_nvfp4v_weights", lambda: (bsq.bsq_quantize_nvfp4v(w_gu, *q_wgu), bsq.bsq_quantize_nvfp4v(w_dn, *q_wdn))),
         ("quant_nvfp4v_x", lambda: bsq.bsq_quantize_nvfp4v(x, *q_x)),
-        ("gemm_fwd_gate_up", lambda: bsq.bsq_grouped_gemm_fwd(q_x, q_wgu, off, 2 * I, Hd, y=gu, workspace=ws_f)),
-        # harness activation H = silu(gate) * up, fused with H's NVFP4v quantization
-        ("swiglu_quant_nvfp4v_h", lambda: bsq.bsq_swiglu_quantize_nvfp4v(gu, h=h, codes=q_h[0], bscale=q_h[1],
-                                                                          rscale=q_h[2])),
+        # gate/up GEMM with the harness activation H = silu(gate) * up in its
+        # epilogue: the gate/up output never reaches HBM
+        ("gemm_fwd_gate_up", lambda: bsq.bsq_grouped_gemm_fwd_swiglu(q_x, q_wgu, off, I, Hd, h=h, workspace=ws_f)),
+        ("quant_nvfp4v_h", lambda: bsq.bsq_quantize_nvfp4v(h, *q_h)),
         ("gemm_fwd_down", lambda: bsq.bsq_grouped_gemm_fwd(q_h, q_wdn, off, Hd, I, y=y, workspace=ws_f)),
         # dY and dGU feed dgrad row-wise and wgrad per expert column: both layouts from one read
         ("quant_mxfp8_dual", lambda: (bsq.bsq_quantize_mxfp8_dual(dy, off, row=q_dy, t=t_dy),
@@ -160,7 +161,7 @@ def build_step(bsq, torch, dev, cfg, counts, seed):
     mxd = lambda r, c: 2 * r * c + 2 * (r * c + r * c // 32)                 # one read, two layouts out
     qbytes = {
         "quant_nvfp4v_weights": nvb(E * 2 * I, Hd) + nvb(E * Hd, I), "quant_nvfp4v_x": nvb(M, Hd),
-        "swiglu_quant_nvfp4v_h": 2 * M * 2 * I + nvb(M, I), "quant_mxfp8_dual": mxd(M, Hd) + mxd(M, 2 * I),
+        "quant_nvfp4v_h": nvb(M, I), "quant_mxfp8_dual": mxd(M, Hd) + mxd(M, 2 * I),
         "quant_mxfp8_colwise_t": mxb(E * Hd, I) + mxb(E * 2 * I, Hd) + mxb(M, I) + mxb(M, Hd),
     }
     return t, stages, flops, qbytes
@@ -259,9 +260,10 @@ def main():
 
     quant = quantize_config2(bsq, torch, dev)
     x, w_gu, w_dn, h, off, ws_f = t["x"], t["w_gu"], t["w_dn"], t["h"], t["off"], t["ws_f"]
-    fwd_mx = fwd_mxfp8_compare(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M,
-                               {k: stage_ms[k] for k in ("gemm_fwd_gate_up", "gemm_fwd_down")}, ws_f)
-    bf16_base = bf16_baseline(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, stage_ms, fwd_mx, ws_f)
+    unfused = unfused_gate_up(bsq, torch, t, off, I, Hd, stage_ms)
+    plain_ms = {"gemm_fwd_gate_up": unfused["gemm_fwd_gate_up_plain_ms"], "gemm_fwd_down": stage_ms["gemm_fwd_down"]}
+    fwd_mx = fwd_mxfp8_compare(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, plain_ms, ws_f)
+    bf16_base = bf16_baseline(bsq, torch, dev, x, w_gu, w_dn, h, off, E, Hd, I, M, plain_ms, fwd_mx, ws_f)
     frozen = frozen_w4a16(bsq, torch, dev, x, h, t["q_wgu"], t["q_wdn"], off, E, Hd, I, M, bf16_base, ws_f)
     del t, stages, x, w_gu, w_dn, h, off, ws_f
     torch.cuda.empty_cache()
@@ -288,11 +290,41 @@ def main():
         "ms_per_step_instrumented": round(ms_step_instr, 4),
         "quantize": quant,
         "config5": cfg5,
+        "gate_up_unfused": unfused,
         "fwd_mxfp8": fwd_mx,
         "bf16_baseline": bf16_base,
         "frozen_w4a16": frozen,
     }
     print(json.dumps(out))
+
+
+def unfused_gate_up(bsq, torch, t, off, I, Hd, stage_ms, reps=10):
+    """The gate/up projection without the fused epilogue, on the same tensors
+    outside the step: the plain NVFP4v GEMM writing gu (bf16 [gate | up]),
+    then the SwiGLU + NVFP4v quantize kernel reading it back.  Median of
+    per-launch HIP events; compared with the step's fused GEMM + quantize of H."""
+    stream = torch.cuda.current_stream()
+    q_x, q_wgu, gu, h, q_h, ws_f = t["q_x"], t["q_wgu"], t["gu"], t["h"], t["q_h"], t["ws_f"]
+
+    def med(fn):
+        for _ in range(2):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        return ts[len(ts) // 2]
+
+    g = med(lambda: bsq.bsq_grouped_gemm_fwd(q_x, q_wgu, off, 2 * I, Hd, y=gu, workspace=ws_f))
+    sq = med(lambda: bsq.bsq_swiglu_quantize_nvfp4v(gu, h=h, codes=q_h[0], bscale=q_h[1], rscale=q_h[2]))
+    fused = stage_ms["gemm_fwd_gate_up"] + stage_ms["quant_nvfp4v_h"]
+    return {"gemm_fwd_gate_up_plain_ms": round(g, 4), "swiglu_quant_nvfp4v_ms": round(sq, 4),
+            "unfused_total_ms": round(g + sq, 4), "fused_total_ms": round(fused, 4),
+            "note": "fused = gate/up GEMM with SwiGLU in its epilogue writing H, then the NVFP4v quantize of H "
+                    "(the step's two stages); unfused = GEMM writing gu, then SwiGLU fused with H's quantize"}
 
 
 def config5_line(bsq, torch, dev, steps=10, warmup=3):
@@ -350,11 +382,13 @@ def quantize_config2(bsq, torch, dev, reps=20):
                        2 * R * C + R * C + R * C // 32 + C * P + C * P // 32),
     }
     stream = torch.cuda.current_stream()
-    # 512 MB written before every timed launch: more than the 256 MB Infinity
-    # Cache, so no launch reads its input (235 MB) from the previous one's cache
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # 512 MB read before every timed launch: more than the 256 MB Infinity
+    # Cache, so no launch finds its input (235 MB) cached by the previous one;
+    # a read leaves clean lines, so the launch pays no write-back of the
+    # eviction pass (the previous launch's outputs are written back during it)
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
     out = {"workload": "quantize: 16384 x 7168 bf16 N(0,1), 72 outlier channels x50",
-           "timing": f"median of {reps} launches, each after a 512 MB write that evicts the 256 MB Infinity Cache; "
+           "timing": f"median of {reps} launches, each after a 512 MB read that evicts the 256 MB Infinity Cache; "
                      "HIP events on the launch stream around the launch alone"}
 
     def timed(fn):
@@ -363,7 +397,7 @@ def quantize_config2(bsq, torch, dev, reps=20):
         ts = []
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i in range(reps):
-            flush.fill_(i & 255)
+            flush.amax()
             ev[i][0].record(stream)
             fn()
             ev[i][1].record(stream)

@@ -41,6 +41,7 @@ _SIGS = {
     "bsq_quantize_mxfp8": ([P, I64, I64, I64, INT, P, I32, P, P, P], INT),
     "bsq_quantize_mxfp8_dual": ([P, I64, I64, I64, P, I32, P, P, P, P, P], INT),
     "bsq_grouped_gemm_fwd": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, ctypes.c_size_t, P], INT),
+    "bsq_grouped_gemm_fwd_swiglu": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, I64, P, ctypes.c_size_t, P], INT),
     "bsq_grouped_gemm_fwd_noalloc": ([P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P], INT),
     "bsq_grouped_gemm_bwd": ([P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, P, INT, P, INT, ctypes.c_uint, P,
                               ctypes.c_size_t, P], INT),
@@ -292,6 +293,35 @@ def bsq_grouped_gemm_fwd(a_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, work
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
     return y
+
+
+def bsq_grouped_gemm_fwd_swiglu(a_q, w_q, offsets, inter, k, h=None, workspace=None, stream=None):
+    """Gate/up grouped GEMM with the SwiGLU activation in its epilogue.
+    a_q = NVFP4v (codes, bscale, rscale) of the expert-sorted activations
+    [m_total, k]; w_q = NVFP4v of the gate/up weights [E*2*inter, k] ([gate;
+    up] rows per expert).  Returns h bf16 [m_total, inter]; the gate/up output
+    is never written."""
+    a_codes, a_bscale, a_rscale = a_q
+    w_codes, w_bscale, w_rscale = w_q
+    _dev(offsets, "offsets", (torch.int32,))
+    E = offsets.numel() - 1
+    m_total = a_codes.shape[0]
+    if w_codes.shape[0] != E * 2 * inter:
+        raise ValueError("weights must hold num_experts * 2 * inter rows")
+    dev = a_codes.device
+    if h is None:
+        h = _empty(stream, (m_total, inter), dtype=torch.bfloat16, device=dev)
+    _dev(h, "h", _BF16)
+    if tuple(h.shape) != (m_total, inter) or (m_total > 1 and h.stride(1) != 1):
+        raise ValueError(f"h must be row-major with shape {(m_total, inter)}")
+    ldh = h.stride(0) if m_total > 1 else inter
+    workspace = _workspace(BSQ_OP_GEMM_FWD, E, m_total, 2 * inter, k, workspace, dev, stream)
+    _check("bsq_grouped_gemm_fwd_swiglu",
+           _lib.bsq_grouped_gemm_fwd_swiglu(_ptr(a_codes), _ptr(a_bscale), _ptr(a_rscale), _ptr(w_codes),
+                                            _ptr(w_bscale), _ptr(w_rscale), _ptr(offsets), E, m_total, inter, k,
+                                            _ptr(h), ldh, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))
+    return h
 
 
 def bsq_grouped_gemm_fwd_noalloc(a_q, w_q, offsets, n, k, y_dtype=BSQ_BF16, y=None, stream=None):

@@ -209,7 +209,31 @@ bsq_status bsq_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_bscale,
     if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, n, k))
         return BSQ_ERR_WORKSPACE_TOO_SMALL;
     return from_hip(bsq::launch_gemm_fwd_nvfp4v(a_codes, a_bscale, a_rscale, w_codes, w_bscale, w_rscale, offsets,
-                                                num_experts, m_total, n, k, y, y_dtype == BSQ_F32 ? 1 : 0,
+                                                num_experts, m_total, n, k, y, y_dtype == BSQ_F32 ? 1 : 0, 0, n,
+                                                static_cast<int32_t*>(workspace), persistent_grid(), stream));
+}
+
+bsq_status bsq_grouped_gemm_fwd_swiglu(const uint8_t* a_codes, const uint8_t* a_bscale, const float* a_rscale,
+                                       const uint8_t* w_codes, const uint8_t* w_bscale, const float* w_rscale,
+                                       const int32_t* offsets, int32_t num_experts, int64_t m_total, int64_t inter,
+                                       int64_t k, void* h_bf16, int64_t ld_h, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    if (num_experts < 1 || m_total < 0 || inter < 0 || k < 0) return BSQ_ERR_INVALID_ARG;
+    if (!offsets || !workspace || !w_codes || !w_bscale || !w_rscale) return BSQ_ERR_INVALID_ARG;
+    if (m_total > 0 && (!a_codes || !a_bscale || !a_rscale || !h_bf16 || ld_h < inter)) return BSQ_ERR_INVALID_ARG;
+    if (num_experts > bsq::MAX_EXPERTS) return BSQ_ERR_UNSUPPORTED;
+    // a 256-column output tile holds 128 gate and the matching 128 up columns
+    if (k == 0 || inter == 0 || k % 64 || inter % 128) return BSQ_ERR_UNSUPPORTED;
+    if (!aligned(a_codes, 16) || !aligned(w_codes, 16) || !aligned(a_bscale, 4) || !aligned(w_bscale, 4) ||
+        !aligned(workspace, 256) || (m_total > 0 && (!aligned(h_bf16, 16) || ld_h % 8)))
+        return BSQ_ERR_UNSUPPORTED;
+    // 32-bit per-tile offsets: 256 rows of codes / scales, 256 rows of H
+    if (256 * (k / 2) >= kMaxBufferOffset || m_total >= (int64_t)1 << 31 || 256 * ld_h * 2 >= kMaxBufferOffset)
+        return BSQ_ERR_UNSUPPORTED;
+    if (workspace_bytes < bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total, 2 * inter, k))
+        return BSQ_ERR_WORKSPACE_TOO_SMALL;
+    return from_hip(bsq::launch_gemm_fwd_nvfp4v(a_codes, a_bscale, a_rscale, w_codes, w_bscale, w_rscale, offsets,
+                                                num_experts, m_total, 2 * inter, k, h_bf16, 0, 1, ld_h,
                                                 static_cast<int32_t*>(workspace), persistent_grid(), stream));
 }
 

@@ -46,6 +46,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// SwiGLU activation between the two forward GEMMs (not on the pages; the
+// plainest DeepSeek-V3-class reading): H = silu(g) * u with silu(g) =
+// g * sigmoid(g), evaluated in binary32 from t = e^-|g| in (0, 1], which never
+// overflows: g / (1 + t) for g >= 0 and (g * t) / (1 + t) for g < 0, so a very
+// negative gate gives the tiny value it should.  t = 2^y with y = -|g| log2(e)
+// comes from the hardware exponential; for y < -126 (t below the binary32
+// normal range) the argument is raised by 64 and the result scaled by 2^-64,
+// so t keeps its subnormal value instead of flushing to zero.  1 / (1 + t),
+// with 1 + t in [1, 2], comes from the hardware reciprocal.  Each step is
+// within a few binary32 ulps (the rounding of y costs |y| 2^-24 relative in
+// t), far below the bf16 rounding of the result: H lies within one bf16 ulp
+// of the exactly rounded value, equal to it except next to a rounding
+// boundary.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float y = -fabsf(g) * 1.44269504f;
+    const bool tiny = y < -126.0f;
+    float t = __builtin_amdgcn_exp2f(tiny ? y + 64.0f : y);
+    t = tiny ? t * 0x1p-64f : t;
+    const float num = g >= 0.0f ? g : g * t;
+    return (num * __builtin_amdgcn_rcpf(1.0f + t)) * u;
+}
+
+// H of two packed bf16 gate values and the matching up values, packed bf16
+// (round to nearest even), low halves first.
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
+    return pack_bf16x2(silu_mul(bf16_lo(gw), bf16_lo(uw)), silu_mul(bf16_hi(gw), bf16_hi(uw)));
+}
+
 // E2M1 codes of two floats into nibbles of byte `sel` of `old`: low nibble
 // from a, high nibble from b.  The hardware conversion rounds to nearest
 // even, saturates to +-6 and keeps the sign of zero; a unit scale leaves the

@@ -198,6 +198,6 @@ hipError_t launch_gemm_bwd_mxfp8(const BwdArgs& args, int grid, hipStream_t s);
 hipError_t launch_gemm_fwd_nvfp4v(const uint8_t* a_codes, const uint8_t* a_bscale, const float* a_rscale,
                                   const uint8_t* w_codes, const uint8_t* w_bscale, const float* w_rscale,
                                   const int32_t* offsets, int E, int64_t m_total, int64_t N, int64_t K, void* y,
-                                  int y_f32, int32_t* plan, int grid, hipStream_t s);
+                                  int y_f32, int swiglu, int64_t ldo, int32_t* plan, int grid, hipStream_t s);
 
 }  // namespace bsq

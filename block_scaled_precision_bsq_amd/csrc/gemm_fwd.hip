@@ -35,6 +35,17 @@
 // next group and, once per super-stage, the ring refill pinned between them
 // by sched_barrier, so VALU, LDS and DMA work runs in the matrix core's
 // shadow.
+//
+// SWIGLU (the gate/up projection with the activation in its epilogue): the
+// weight stack holds [gate; up] rows per expert (N = 2 I, I % 128 == 0), and
+// output tile nt takes gate rows [128 nt, +128) as its columns 0..127 and the
+// matching up rows [I + 128 nt, +128) as columns 128..255 (waves 0-1 and 2-3
+// load the two halves from their own base rows).  The epilogue rounds each
+// scaled gate and up value to bf16 -- the values the plain GEMM would store --
+// and writes H = swiglu_pair(gate, up) for H columns [128 nt, +128): the
+// gate/up output itself never reaches memory.  The "Cursor Composer 2 report
+// deep dive", section 1, places the per-token scaling cost in the quantize
+// and GEMM epilogue; here the activation joins it.
 #include "device_common.h"
 #include "gemm_common.h"
 #include "gemm_pipe.h"
@@ -66,6 +77,7 @@ struct FwdArgs {
     const uint8_t* w_codes; const uint8_t* w_bscale; const float* w_rscale;
     const int32_t* offsets; int E; int64_t N; int64_t K;
     void* y; int y_f32; int32_t* plan;
+    int64_t ldo;  // SWIGLU: row pitch (elements) of the bf16 H output
 };
 
 // Raw LDS data of one 64-element group: 16 code bytes and one scale dword per
@@ -94,8 +106,9 @@ __device__ __forceinline__ void dequant_half(half8& out, uint32_t w, _Float16 s)
     out[4 * H + 3] = p1[1];
 }
 
-template <bool OUT_F32>
+template <bool OUT_F32, bool SWIGLU>
 __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
+    static_assert(!(OUT_F32 && SWIGLU), "the activation output is bf16");
     extern __shared__ __align__(16) uint8_t smem_raw[];
     __shared__ int s_tile;
 
@@ -162,8 +175,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
         const int64_t m_base = uniform_i64(off0 + (int64_t)mt * FWD_BM);
         const int rows_a = __builtin_amdgcn_readfirstlane((int)min((int64_t)FWD_BM, off1 - m_base));
         const int64_t n_base = uniform_i64((int64_t)nt * FWD_BN);
-        const int rows_b = __builtin_amdgcn_readfirstlane((int)min((int64_t)FWD_BN, p.N - n_base));
-        const int64_t wrow = uniform_i64((int64_t)e * p.N + n_base);
+        // first weight row of this wave's B rows (SWIGLU: waves 2-3 take the up half)
+        const int64_t wrow = SWIGLU ? uniform_i64((int64_t)e * p.N + 128 * (int64_t)nt + (wave >= 2 ? p.N / 2 - 128 : 0))
+                                    : uniform_i64((int64_t)e * p.N + n_base);
+        const int rows_b = SWIGLU ? FWD_BN : __builtin_amdgcn_readfirstlane((int)min((int64_t)FWD_BN, p.N - n_base));
         const i32x4 dA = make_desc(uniform_ptr(p.a_codes + m_base * (int64_t)KB));
         const i32x4 dB = make_desc(uniform_ptr(p.w_codes + wrow * (int64_t)KB));
         const i32x4 dAs = make_desc(uniform_ptr(p.a_bscale + m_base * (int64_t)KS));
@@ -301,10 +316,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
         // puts the two lane halves on disjoint banks.
         {
             constexpr uint32_t EP = 1056;
-            const __amdgpu_buffer_rsrc_t rc = make_rsrc(uniform_ptr(reinterpret_cast<char*>(p.y) +
-                                                                    (m_base * p.N + n_base) * esz),
-                                                        0x7FFFFFFFu);
-            const uint32_t ldcb = (uint32_t)p.N * (uint32_t)esz;
+            // SWIGLU: the tile's H columns start at 128 nt of rows of p.ldo elements
+            const __amdgpu_buffer_rsrc_t rc =
+                make_rsrc(uniform_ptr(reinterpret_cast<char*>(p.y) +
+                                      (SWIGLU ? (m_base * p.ldo + 128 * (int64_t)nt) * 2 : (m_base * p.N + n_base) * esz)),
+                          0x7FFFFFFFu);
+            const uint32_t ldcb = SWIGLU ? (uint32_t)p.ldo * 2u : (uint32_t)p.N * (uint32_t)esz;
             __attribute__((address_space(3))) uint8_t* st = (__attribute__((address_space(3))) uint8_t*)(smem_raw);
             const __attribute__((address_space(3))) float* rsa =
                 (const __attribute__((address_space(3))) float*)(st + offsetof(FwdSmem, rs_a));
@@ -327,7 +344,34 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
                 wait_lgkmcnt0();
                 block_barrier();
                 // staged row r (0..127) is tile row (r / 64) * 128 + 64 * pass + r % 64
-                if constexpr (OUT_F32) {
+                if constexpr (SWIGLU) {
+#pragma unroll 2
+                    for (int it = 0; it < 8; ++it) {
+                        const int c = it * 256 + tid;  // 16 chunks of 8 H columns per row
+                        const int r = c >> 4, cc = c & 15;
+                        const int row = (r >> 6) * 128 + 64 * pass + (r & 63);
+                        const uint32_t ro = (uint32_t)r * EP + 32u * cc;
+                        const u32x4 g0 = *(const __attribute__((address_space(3))) u32x4*)(st + ro);
+                        const u32x4 g1 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + 16u);
+                        const u32x4 u0 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + 512u);
+                        const u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + 528u);
+                        const float sa = rsa[row];
+                        float gv[8], uv[8];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            gv[q] = (__uint_as_float(g0[q]) * sa) * rsw[8 * cc + q];
+                            gv[4 + q] = (__uint_as_float(g1[q]) * sa) * rsw[8 * cc + 4 + q];
+                            uv[q] = (__uint_as_float(u0[q]) * sa) * rsw[128 + 8 * cc + q];
+                            uv[4 + q] = (__uint_as_float(u1[q]) * sa) * rsw[128 + 8 * cc + 4 + q];
+                        }
+                        u32x4 y;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            y[q] = swiglu_pair(pack_bf16x2(gv[2 * q], gv[2 * q + 1]), pack_bf16x2(uv[2 * q], uv[2 * q + 1]));
+                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, row < rows_a ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB,
+                                                               0, OUT_STORE_NT);
+                    }
+                } else if constexpr (OUT_F32) {
 #pragma unroll 4
                     for (int it = 0; it < 32; ++it) {
                         const int c = it * 256 + tid;  // 64 chunks of 4 columns per row
@@ -382,28 +426,30 @@ size_t fwd_smem_bytes() { return sizeof(FwdSmem); }
 hipError_t launch_gemm_fwd_nvfp4v(const uint8_t* a_codes, const uint8_t* a_bscale, const float* a_rscale,
                                   const uint8_t* w_codes, const uint8_t* w_bscale, const float* w_rscale,
                                   const int32_t* offsets, int E, int64_t m_total, int64_t N, int64_t K, void* y,
-                                  int y_f32, int32_t* plan, int grid, hipStream_t s) {
+                                  int y_f32, int swiglu, int64_t ldo, int32_t* plan, int grid, hipStream_t s) {
     const int NT = (int)((N + FWD_BN - 1) / FWD_BN);
     hipError_t err = launch_plan(offsets, E, m_total, PLAN_RAGGED_ROWS, FWD_BM, NT, 1, plan, s);
     if (err != hipSuccess) return err;
     static bool attr_set = false;  // idempotent; racing writers set the same value
     if (!attr_set) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)(sizeof(FwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
-        if (err != hipSuccess) return err;
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)(sizeof(FwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
-        if (err != hipSuccess) return err;
+        const void* ks[3] = {reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<true, false>),
+                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false, false>),
+                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false, true>)};
+        for (const void* k : ks) {
+            err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)(sizeof(FwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
+            if (err != hipSuccess) return err;
+        }
         attr_set = true;
     }
-    FwdArgs p{a_codes, a_bscale, a_rscale, w_codes, w_bscale, w_rscale, offsets, E, N, K, y, y_f32, plan};
+    FwdArgs p{a_codes, a_bscale, a_rscale, w_codes, w_bscale, w_rscale, offsets, E, N, K, y, y_f32, plan, ldo};
     const size_t lds = sizeof(FwdSmem) + lds_table_bytes(E);
-    if (y_f32)
-        hipLaunchKernelGGL(k_gemm_fwd_nvfp4v<true>, dim3(grid), dim3(256), lds, s, p);
+    if (swiglu)
+        hipLaunchKernelGGL((k_gemm_fwd_nvfp4v<false, true>), dim3(grid), dim3(256), lds, s, p);
+    else if (y_f32)
+        hipLaunchKernelGGL((k_gemm_fwd_nvfp4v<true, false>), dim3(grid), dim3(256), lds, s, p);
     else
-        hipLaunchKernelGGL(k_gemm_fwd_nvfp4v<false>, dim3(grid), dim3(256), lds, s, p);
+        hipLaunchKernelGGL((k_gemm_fwd_nvfp4v<false, false>), dim3(grid), dim3(256), lds, s, p);
     return hipGetLastError();
 }
 

@@ -34,22 +34,10 @@ namespace bsq {
 // costs one binary64 division per 16 elements instead of 16 fp32 divisions.
 //
 // SWIGLU: x holds rows [gate | up] of 2 * cols bf16 and the row quantized is
-// H = bf16_RNE(silu(gate) * up) (the activation between the two forward
-// GEMMs; it is not on the pages).  silu(g) = g * sigmoid(g) is evaluated in
-// binary32 from t = e^-|g|, which never overflows: g / (1 + t) for g >= 0 and
-// (g * t) / (1 + t) for g < 0, so a very negative gate gives the tiny value it
-// should instead of g / inf.  H is also written to h (when non-null), so the
-// backward pass can quantize the same values; the quantization of H is the
-// one above, byte for byte.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    const float t = expf(-fabsf(g));
-    const float num = g >= 0.0f ? g : g * t;
-    return (num / (1.0f + t)) * u;
-}
-
-__device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
-    return pack_bf16x2(silu_mul(bf16_lo(gw), bf16_lo(uw)), silu_mul(bf16_hi(gw), bf16_hi(uw)));
-}
+// H = swiglu_pair(gate, up) (device_common.h; the activation between the two
+// forward GEMMs, not on the pages).  H is also written to h (when non-null),
+// so the backward pass can quantize the same values; the quantization of H
+// is the one above, byte for byte.
 
 // FASTDIV (ablation only, not the method): every division of the row
 // quantizer -- A / 2688, 448 a_b / A and x / d_b -- is replaced by the

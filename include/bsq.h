@@ -70,8 +70,10 @@ typedef struct ihipStream_t* hipStream_t;
 
 /* 3: COLWISE_T segments start on 128-column boundaries (P changed);
  * added bsq_quantize_mxfp8_dual and bsq_grouped_gemm_w4a16.
- * 4: added bsq_grouped_gemm_fwd_noalloc. */
-#define BSQ_ABI_VERSION 4
+ * 4: added bsq_grouped_gemm_fwd_noalloc.
+ * 5: added bsq_grouped_gemm_fwd_swiglu; the SwiGLU activation's reciprocal
+ *    (1 + e^-|g|)^-1 comes from the hardware reciprocal. */
+#define BSQ_ABI_VERSION 5
 
 typedef enum {
     BSQ_OK = 0,
@@ -245,6 +247,33 @@ bsq_status bsq_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_bscale,
                                 const int32_t* offsets, int32_t num_experts, int64_t m_total, int64_t n,
                                 int64_t k, void* y, bsq_dtype y_dtype, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * bsq_grouped_gemm_fwd_swiglu -- the gate/up projection of the MoE forward
+ * with the activation in the GEMM epilogue ("Cursor Composer 2 report deep
+ * dive", section 1: the per-token scale is applied in the GEMM epilogue;
+ * "Composer 2 Technical Report", section 6.1).  With gu = the bf16 output
+ * bsq_grouped_gemm_fwd would write for these operands ([gate | up] columns,
+ * 2*inter of them), it writes only
+ *   h[m][j] = bf16_RNE(silu(gu[m][j]) * gu[m][inter + j]),   j < inter,
+ * with silu evaluated in binary32 (within one bf16 ulp of the exact value;
+ * bit for bit what bsq_swiglu_quantize_nvfp4v writes as h from that gu).  gu
+ * itself never reaches memory.  Quantize h with bsq_quantize_nvfp4v for the
+ * down projection.
+ *   a_*: NVFP4v of the expert-sorted activations [m_total][k].
+ *   w_*: NVFP4v of the gate/up weights [num_experts][2*inter][k]: rows
+ *   e*2*inter + j are gate row j, rows e*2*inter + inter + j up row j.
+ *   h_bf16 [m_total][ld_h] bf16, ld_h >= inter, ld_h % 8 == 0, 16-byte aligned.
+ *   inter % 128 == 0, k % 64 == 0, num_experts >= 1.
+ *   workspace >= bsq_workspace_size(BSQ_OP_GEMM_FWD, num_experts, m_total,
+ *   2*inter, k) bytes, 256-byte aligned.
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP.
+ */
+bsq_status bsq_grouped_gemm_fwd_swiglu(const uint8_t* a_codes, const uint8_t* a_bscale, const float* a_rscale,
+                                       const uint8_t* w_codes, const uint8_t* w_bscale, const float* w_rscale,
+                                       const int32_t* offsets, int32_t num_experts, int64_t m_total, int64_t inter,
+                                       int64_t k, void* h_bf16, int64_t ld_h, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * bsq_grouped_gemm_fwd_noalloc -- bsq_grouped_gemm_fwd without a workspace

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(bsq):
 
 
 def test_version_and_helpers(bsq):
-    assert bsq.ABI_VERSION == 4
+    assert bsq.ABI_VERSION == 5
     assert bsq.bsq_colwise_padded_cols(32, 32768) == 128 * (32 + 256)
     assert bsq.bsq_colwise_padded_cols(3, 0) == 384
     assert bsq.bsq_colwise_padded_cols(2, 129) == 128 * (2 + 2)
@@ -122,3 +122,19 @@ def test_noalloc_host_checks(bsq):
     assert f(*args(4097)) == bsq.BSQ_ERR_UNSUPPORTED
     assert f(*args(0)) == bsq.BSQ_ERR_INVALID_ARG
     assert f(*args(-3)) == bsq.BSQ_ERR_INVALID_ARG
+
+
+def test_gemm_swiglu_host_checks(bsq):
+    """The fused gate/up + SwiGLU GEMM needs inter % 128 == 0 (a 256-column
+    tile holds 128 gate and the matching 128 up columns) and a valid H pitch."""
+    f = bsq._lib.bsq_grouped_gemm_fwd_swiglu
+    need = bsq.bsq_workspace_size(bsq.BSQ_OP_GEMM_FWD, 4, 64, 256, 128)
+    args = lambda inter, k, ldh, ws=need, E=4, h=FAKE: (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, E, 64, inter, k,
+                                                        h, ldh, FAKE, ws, None)
+    assert f(*args(64, 128, 64)) == bsq.BSQ_ERR_UNSUPPORTED      # inter % 128
+    assert f(*args(128, 96, 128)) == bsq.BSQ_ERR_UNSUPPORTED     # k % 64
+    assert f(*args(128, 128, 100)) == bsq.BSQ_ERR_INVALID_ARG    # ld_h < inter
+    assert f(*args(128, 128, 132)) == bsq.BSQ_ERR_UNSUPPORTED    # ld_h % 8
+    assert f(*args(128, 128, 128, h=None)) == bsq.BSQ_ERR_INVALID_ARG
+    assert f(*args(128, 128, 128, E=0)) == bsq.BSQ_ERR_INVALID_ARG
+    assert f(*args(128, 128, 128, ws=need - 1)) == bsq.BSQ_ERR_WORKSPACE_TOO_SMALL

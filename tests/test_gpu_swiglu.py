@@ -58,8 +58,10 @@ def _check(orc, bsq, gu_bits, h_got, q_got):
             * rscale[r][:, None].astype(np.float64)
         href = bf16_bits_to_f32(h_ref[r]).astype(np.float64)
         hgot = bf16_bits_to_f32(hg[r]).astype(np.float64)
-        # |x - q d_b| <= d_b (half the widest E2M1 gap; d_b itself is rounded to binary32)
-        assert np.all(np.abs(deq - href) <= d_b * (1 + 1e-6) + np.abs(hgot - href))
+        # |x - q d_b| <= d_b (half the widest E2M1 gap; d_b itself is rounded to
+        # binary32); a block whose scale byte underflows to 0 (d_b = 0) is all zero
+        within = np.abs(deq - href) <= d_b * (1 + 1e-6) + np.abs(hgot - href)
+        assert np.all(np.where(d_b == 0, deq == 0, within))
 
 
 @pytest.mark.parametrize("rows,inter", [(1, 16), (37, 2048), (133, 1040), (64, 4096), (5, 16384)])
@@ -86,13 +88,21 @@ def test_swiglu_quantize_matches_standalone_quantizer(bsq_gpu):
 
 def test_swiglu_quantize_strided_and_edges(orc, bsq_gpu):
     """Strided gate/up rows (a column slice of a wider matrix), an all-zero
-    row, zero gates (H = 0 exactly) and huge negative gates (silu -> -0)."""
+    row, zero gates (H = 0 exactly), huge negative gates (silu -> -0), gates
+    whose e^-|g| is subnormal in binary32 and a sweep of gates over
+    [-100, 100]."""
     rng = rng_for(4, salt=11)
     inter = 256
     wide = _gu(rng, 24, inter + 64)               # [24][2*inter + 128]
     wide[0] = 0
     wide[1, :inter] = 0
     wide[2, :inter] = f32_to_bf16_bits(np.full(inter, -200.0, np.float32))
+    # gates where e^-|g| is below the binary32 normal range (|g| > 87.3) while
+    # g e^g u is still a normal or subnormal bf16 value (moderate u: a huge u
+    # would lift into range a product whose e^g binary32 cannot carry)
+    wide[3, :inter] = f32_to_bf16_bits(np.linspace(-100.0, -80.0, inter).astype(np.float32))
+    wide[3, inter:2 * inter] = f32_to_bf16_bits(np.linspace(0.5, 4.0, inter).astype(np.float32))
+    wide[4, :inter] = f32_to_bf16_bits(np.linspace(-100.0, 100.0, inter).astype(np.float32))
     gu = np.ascontiguousarray(wide[:, :2 * inter])
     dev = _dev(wide)[:, :2 * inter]
     h, codes, bscale, rscale = bsq_gpu.bsq_swiglu_quantize_nvfp4v(dev)
