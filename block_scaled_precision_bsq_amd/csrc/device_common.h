@@ -27,6 +27,17 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Streaming stores of outputs written once (non-temporal hint); used where a
+// wave's stores cover whole 128-byte lines (partial-line and byte stores stay
+// ordinary stores, which the L2 merges).
+__device__ __forceinline__ void st_stream16(void* p, uint4 v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st_stream8(void* p, uint2 v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

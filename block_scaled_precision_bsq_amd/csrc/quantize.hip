@@ -132,7 +132,7 @@ __device__ __forceinline__ void nvfp4v_encode_row(const uint4 (&v)[BPL][2], cons
         if (b >= nb) continue;
         const uint32_t S = rmax ? nvfp4v_block_scale<FASTDIV>(bmax[i], A) : 0u;
         br[b] = (uint8_t)S;
-        *reinterpret_cast<uint2*>(cr + 8 * b) = rmax ? nvfp4v_block_codes<FASTDIV>(v[i], S, s_row) : make_uint2(0, 0);
+        st_stream8(cr + 8 * b, rmax ? nvfp4v_block_codes<FASTDIV>(v[i], S, s_row) : make_uint2(0, 0));
     }
 }
 
@@ -168,8 +168,8 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restr
                                      swiglu_pair(v[i][1].z, u1.z), swiglu_pair(v[i][1].w, u1.w));
                 if (h) {
                     uint4* ph = reinterpret_cast<uint4*>(h + row * ldh + 16 * b);
-                    ph[0] = v[i][0];
-                    ph[1] = v[i][1];
+                    st_stream16(ph, v[i][0]);
+                    st_stream16(ph + 1, v[i][1]);
                 }
             }
         } else {
@@ -228,13 +228,15 @@ __device__ __forceinline__ MxBlock mx_encode(const uint32_t (&w)[16]) {
     return r;
 }
 
-// Row-wise MXFP8.  A workgroup owns 128 rows x 32 blocks (1024 columns);
+// Row-wise MXFP8.  A workgroup owns 32 rows x 32 blocks (1024 columns) --
+// small enough that the grid (3584 workgroups for 16384 x 7168) spreads
+// evenly over the compute units;
 // neighbouring threads take neighbouring blocks of a row (64-byte loads and
 // 32-byte code stores, contiguous across a wave).  Scales are block-major, so
 // a thread's scale byte is `rows` bytes away from its neighbour's: the bytes
-// are gathered in LDS as [block][row] and leave as one 128-byte run per block
+// are gathered in LDS as [block][row] and leave as one 32-byte run per block
 // (16-byte stores when every run is 16-byte aligned, bytes otherwise).
-constexpr int MXR_ROWS = 128;
+constexpr int MXR_ROWS = 32;
 constexpr int MXR_BLK = 32;
 constexpr int MXR_PITCH = MXR_ROWS + 8;  // bytes per block row in LDS (bank spread)
 
@@ -292,15 +294,18 @@ __global__ __launch_bounds__(256) void k_quantize_mxfp8_rowwise(const uint16_t* 
             const MxBlock r = mx_encode(w[u]);
             if (okb & (row < rows)) {
                 uint4* o = reinterpret_cast<uint4*>(codes + row * (int64_t)cols + 32 * b);
-                o[0] = r.c0;
-                o[1] = r.c1;
+                st_stream16(o, r.c0);
+                st_stream16(o + 1, r.c1);
                 sb[bl * MXR_PITCH + rl] = (uint8_t)r.sbyte;
             }
         }
     }
     __syncthreads();
-    // block bl2 = t / 8 leaves as bytes [16 * (t % 8), +16) of its 128-row run
-    const int bl2 = t >> 3, q = t & 7;
+    // block bl2 = t / CPB leaves as bytes [16 * (t % CPB), +16) of its run of
+    // MXR_ROWS rows
+    constexpr int CPB = MXR_ROWS / 16;
+    if (t >= MXR_BLK * CPB) return;
+    const int bl2 = t / CPB, q = t % CPB;
     const int bb = b0 + bl2;
     const int64_t rr = r0 + 16 * q;
     if (bb >= nb || rr >= rows) return;
