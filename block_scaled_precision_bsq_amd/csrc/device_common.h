@@ -33,6 +33,7 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
 __device__ __forceinline__ void st_stream16(void* p, uint4 v) {
     __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
 }
+__device__ __forceinline__ void st_stream4(void* p, uint32_t v) { __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p)); }
 __device__ __forceinline__ void st_stream8(void* p, uint2 v) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
@@ -41,12 +42,15 @@ __device__ __forceinline__ void st_stream8(void* p, uint2 v) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// |bf16| maximum of the two halves of w and of m (bit patterns; valid for
-// non-NaN values because magnitudes order like their bit patterns).
-__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t m, uint32_t w) {
-    uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
-    return max(m, max(lo, hi));
+// Per-half |bf16| maxima of m (two 16-bit magnitudes) and w: one mask and
+// one packed 16-bit max (magnitudes of non-NaN bf16 order like their bits).
+__device__ __forceinline__ uint32_t absmax2_bf16(uint32_t m, uint32_t w) {
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m),
+                                                                  __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu)));
 }
+// The larger of the two 16-bit halves of m.
+__device__ __forceinline__ uint32_t fold_max16(uint32_t m) { return max(m & 0xFFFFu, m >> 16); }
 
 // Two floats -> packed bf16 pair, a in the low half, rounded to nearest even
 // by the hardware conversion (v_cvt_pk_bf16_f32).
@@ -104,14 +108,6 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
     d = __builtin_amdgcn_fmed3f(d, 448.0f, -448.0f);
     uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-}
-
-// Exact value of an E4M3 byte with clear sign bit (0..0x7E).
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-    uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    float normal = __uint_as_float(((e + 120u) << 23) | (m << 20));
-    float sub = (float)m * 0x1p-9f;
-    return e ? normal : sub;
 }
 
 // Wave-wide maximum (wave64) of a non-negative value's bit pattern.

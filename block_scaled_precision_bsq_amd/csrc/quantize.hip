@@ -57,15 +57,20 @@ __device__ __forceinline__ float rcp_approx(float b) {
 // row with |x| maximum A > 0: S_b = E4M3_RNE(RN32(448 * a_b / A)).  The
 // numerator and denominator are exact; for a_b > 2^119, where 448*a_b could
 // overflow, both are scaled by 2^-9 (0.875*a_b and A*2^-9: exact, finite,
-// same quotient).
+// same quotient).  The quotient is RN32(num * RN64(1 / den)), as for x / d_b
+// below; invA = RN64(1 / A) is computed once per row, and RN64(1 / (A 2^-9))
+// = invA * 2^9 exactly.
 template <bool FASTDIV>
-__device__ __forceinline__ uint32_t nvfp4v_block_scale(uint32_t amax_b, float A) {
+__device__ __forceinline__ uint32_t nvfp4v_block_scale(uint32_t amax_b, float A, double invA) {
     const float ab = __uint_as_float(amax_b << 16);
-    float num, den;
-    if (ab <= 0x1p119f) { num = 448.0f * ab;  den = A; }
-    else                { num = 0.875f * ab;  den = A * 0x1p-9f; }
-    const float t = FASTDIV ? num * rcp_approx(den) : num / den;  // in [0, 448]
-    return e4m3x4(t, 0.0f, 0.0f, 0.0f) & 0xFFu;
+    const bool big = ab > 0x1p119f;
+    const float num = big ? 0.875f * ab : 448.0f * ab;
+    float t;
+    if constexpr (FASTDIV)
+        t = num * rcp_approx(big ? A * 0x1p-9f : A);
+    else
+        t = (float)((double)num * (big ? invA * 0x1p9 : invA));  // in [0, 448]
+    return __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(t, 448.0f, -448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
 // E2M1 codes (8 bytes) of one 16-element block with scale byte S in a row
@@ -73,7 +78,7 @@ __device__ __forceinline__ uint32_t nvfp4v_block_scale(uint32_t amax_b, float A)
 // (all zero when d_b == 0).
 template <bool FASTDIV>
 __device__ __forceinline__ uint2 nvfp4v_block_codes(const uint4 (&v)[2], uint32_t S, float s_row) {
-    const float d = e4m3_value(S) * s_row;
+    const float d = __builtin_amdgcn_cvt_f32_fp8((int)S, 0) * s_row;  // exact E4M3 value
     uint2 out = make_uint2(0, 0);
     if (d != 0.0f) {
         float q[16];
@@ -126,11 +131,12 @@ __device__ __forceinline__ void nvfp4v_encode_row(const uint4 (&v)[BPL][2], cons
     const float s_row = nvfp4v_row_scale<FASTDIV>(rmax);
     if (lane == 0) *rs = s_row;
     const float A = __uint_as_float(rmax << 16);
+    const double invA = FASTDIV || !rmax ? 0.0 : 1.0 / (double)A;
 #pragma unroll
     for (int i = 0; i < BPL; ++i) {
         const int b = lane + 64 * i;
         if (b >= nb) continue;
-        const uint32_t S = rmax ? nvfp4v_block_scale<FASTDIV>(bmax[i], A) : 0u;
+        const uint32_t S = rmax ? nvfp4v_block_scale<FASTDIV>(bmax[i], A, invA) : 0u;
         br[b] = (uint8_t)S;
         st_stream8(cr + 8 * b, rmax ? nvfp4v_block_codes<FASTDIV>(v[i], S, s_row) : make_uint2(0, 0));
     }
@@ -177,12 +183,12 @@ __global__ __launch_bounds__(256) void k_quantize_nvfp4v(const uint16_t* __restr
             v[i][1] = make_uint4(0, 0, 0, 0);
         }
         uint32_t m = 0;
-        m = absmax_bf16x2(m, v[i][0].x); m = absmax_bf16x2(m, v[i][0].y);
-        m = absmax_bf16x2(m, v[i][0].z); m = absmax_bf16x2(m, v[i][0].w);
-        m = absmax_bf16x2(m, v[i][1].x); m = absmax_bf16x2(m, v[i][1].y);
-        m = absmax_bf16x2(m, v[i][1].z); m = absmax_bf16x2(m, v[i][1].w);
-        bmax[i] = m;
-        rmax = max(rmax, m);
+        m = absmax2_bf16(m, v[i][0].x); m = absmax2_bf16(m, v[i][0].y);
+        m = absmax2_bf16(m, v[i][0].z); m = absmax2_bf16(m, v[i][0].w);
+        m = absmax2_bf16(m, v[i][1].x); m = absmax2_bf16(m, v[i][1].y);
+        m = absmax2_bf16(m, v[i][1].z); m = absmax2_bf16(m, v[i][1].w);
+        bmax[i] = fold_max16(m);
+        rmax = max(rmax, bmax[i]);
     }
     uint8_t* cr = codes + row * (int64_t)(cols >> 1);
     uint8_t* br = bscale + row * (int64_t)nb;
@@ -200,7 +206,8 @@ struct MxBlock {
 __device__ __forceinline__ MxBlock mx_encode(const uint32_t (&w)[16]) {
     uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) m = absmax_bf16x2(m, w[j]);
+    for (int j = 0; j < 16; ++j) m = absmax2_bf16(m, w[j]);
+    m = fold_max16(m);
     MxBlock r;
     if (m == 0) {
         r.c0 = make_uint4(0, 0, 0, 0);
