@@ -20,6 +20,7 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef int int8v __attribute__((ext_vector_type(8)));
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte streaming load (data read once: nontemporal hint).
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {

@@ -21,7 +21,10 @@
 // 4 x 4 MFMA tiles, fp32 accumulators in AGPRs).  K runs in super-stages of
 // 256 elements: 128 code bytes + 16 scale bytes per row, moved by
 // buffer-to-LDS DMA (whole 128-byte lines) into a 2-slot ring, refilled once
-// per super-stage with 15 MFMA k steps of latency to spare.
+// per super-stage with 15 MFMA k steps of latency to spare.  The refill slot
+// runs on across tile boundaries: two super-stages before a tile ends it
+// starts fetching the next tile, so a tile begins with its first two
+// super-stages in LDS and no DMA wait.
 //
 // k order inside a 64-element group: the MFMA takes 8 k values per lane from
 // lane group g = lane / 32.  Lane g of a row takes the group's code bytes
@@ -30,22 +33,32 @@
 // The two 16-element scale blocks a lane touches in a group are bytes 2g and
 // 2g + 1 of the row's scale dword for that group.
 //
+// Output columns: lane l of MFMA tile j reads the B row at ring position
+// 32 j + l of its wave's 128 rows, and the DMA places there output column
+// 4 l + j, so a lane ends the tile with four adjacent columns of every row
+// it holds.  The epilogue scales and rounds them in registers and stores
+// them directly (each store instruction covers two rows of 256 contiguous
+// bytes), with no LDS staging and no barrier.
+//
 // Schedule: each k step issues its 16 MFMAs with the dequantization of the
 // next step (8 fragments, half a fragment per MFMA), the LDS reads of the
 // next group and, once per super-stage, the ring refill pinned between them
 // by sched_barrier, so VALU, LDS and DMA work runs in the matrix core's
-// shadow.
+// shadow.  The loop body has no branches: a branch splits the schedule into
+// blocks, and the compiler then sinks each step's dequantization past it,
+// next to the MFMAs that wait for it.
 //
 // SWIGLU (the gate/up projection with the activation in its epilogue): the
-// weight stack holds [gate; up] rows per expert (N = 2 I, I % 128 == 0), and
-// output tile nt takes gate rows [128 nt, +128) as its columns 0..127 and the
-// matching up rows [I + 128 nt, +128) as columns 128..255 (waves 0-1 and 2-3
-// load the two halves from their own base rows).  The epilogue rounds each
-// scaled gate and up value to bf16 -- the values the plain GEMM would store --
-// and writes H = swiglu_pair(gate, up) for H columns [128 nt, +128): the
-// gate/up output itself never reaches memory.  The "Cursor Composer 2 report
-// deep dive", section 1, places the per-token scaling cost in the quantize
-// and GEMM epilogue; here the activation joins it.
+// weight stack holds [gate; up] rows per expert (N = 2 I, I % 128 == 0).
+// Output tile nt covers H columns [128 nt, +128); wave column wn takes H
+// columns 64 wn + 0..63, and its MFMA tiles j = 0, 1 read the gate rows and
+// j = 2, 3 the matching up rows of columns 64 wn + 2 l + (j & 1).  Each lane
+// thus holds gate and up of two adjacent H columns; the epilogue rounds each
+// scaled value to bf16 -- the values the plain GEMM would store -- and
+// writes H = swiglu_pair(gate, up): the gate/up output never reaches memory.
+// The "Cursor Composer 2 report deep dive", section 1, places the per-token
+// scaling cost in the quantize and GEMM epilogue; here the activation joins
+// it.
 #include "device_common.h"
 #include "gemm_common.h"
 #include "gemm_pipe.h"
@@ -53,6 +66,9 @@
 #include <stddef.h>
 
 namespace bsq {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int FWD_BM = 256;
 constexpr int FWD_BN = 256;
@@ -68,8 +84,11 @@ struct FwdSmem {
     uint8_t b[2][FS_CODE_TILE];
     uint8_t sa[2][FS_SCALE_TILE];
     uint8_t sb[2][FS_SCALE_TILE];
-    float rs_a[FWD_BM];  // per-token decode scales of the tile's rows
-    float rs_w[FWD_BN];  // per-output-channel decode scales of the tile's columns
+    // Per-token decode scales of the tile's rows and per-output-channel
+    // scales of its columns, double-buffered: the next tile's land while the
+    // current tile's epilogue reads its own.
+    float rs_a[2][FWD_BM];
+    float rs_w[2][FWD_BN];
 };
 
 struct FwdArgs {
@@ -159,71 +178,148 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     __syncthreads();
     int tile = __builtin_amdgcn_readfirstlane(s_tile);  // uniform: keeps tile state in SGPRs
 
+    // State of the tile whose operands are in flight (uniform).  B rows reach
+    // LDS permuted: ring position 128 wn + 32 j + l (the row that lane l of
+    // wave column wn reads for MFMA tile j) holds
+    //   plain:  output column 128 wn + 4 l + j,
+    //   SWIGLU: gate (j < 2) or up (j >= 2) row of H column 64 wn + 2 l + (j & 1),
+    // so each lane ends a tile holding four adjacent output columns of every
+    // row it owns (SWIGLU: gate and up of two adjacent H columns) and the
+    // epilogue stores straight from the accumulators.  For DMA wave w the
+    // position's row splits into a wave term, a lane term and an instruction
+    // term (see issue_part).
+    int64_t m_base = 0, n_base = 0;
+    int rows_a = 0, rows_b = 0, nt = 0;
+    i32x4 dA = {}, dB = {}, dAs = {}, dBs = {};
+    const float* rs_w_src = nullptr;
+    const int bw0 = SWIGLU ? 64 * (wave >> 1) : 128 * (wave >> 1) + 2 * (wave & 1);  // local B row, wave term
+    // Per-lane DMA offsets at k = 0 (codes: row part only, the chunk comes
+    // from vch0 / vch1).  Rows past the tile's valid rows fall outside the
+    // descriptor's byte range and read as zero.
+    const uint32_t vra = (uint32_t)drow0 * KB;
+    const uint32_t vrb = (uint32_t)((SWIGLU ? 2 : 4) * (lane >> 3)) * KB;
+    const uint32_t vsa = (uint32_t)srow0 * KS + 4 * sdw;
+    const uint32_t vsb = (uint32_t)((SWIGLU ? 2 : 4) * (lane >> 2)) * KS + 4 * sdw;
+    const uint32_t vch0 = 16 * dch0, vch1 = 16 * dch1;
+
+    uint32_t par = 0;  // ring slot of the current tile's super-stage 0
+    int rb = 0;        // scale buffer of the current tile
+    auto setup = [&](int t) {
+        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, t, lane);
+        const int e = tr.e;
+        const int64_t off0 = tr.off0, off1 = tr.off1;
+        int mt;
+        grouped_tile(tr.local, (int)((off1 - off0 + FWD_BM - 1) / FWD_BM), NT, mt, nt);
+        m_base = uniform_i64(off0 + (int64_t)mt * FWD_BM);
+        rows_a = __builtin_amdgcn_readfirstlane((int)min((int64_t)FWD_BM, off1 - m_base));
+        n_base = uniform_i64((int64_t)nt * FWD_BN);
+        rows_b = SWIGLU ? FWD_BN : __builtin_amdgcn_readfirstlane((int)min((int64_t)FWD_BN, p.N - n_base));
+        // first weight row of this wave's DMA rows (SWIGLU: odd waves fetch up rows)
+        const int64_t wrow = SWIGLU ? uniform_i64((int64_t)e * p.N + ((wave & 1) ? p.N / 2 : 0) + 128 * (int64_t)nt + bw0)
+                                    : uniform_i64((int64_t)e * p.N + n_base + bw0);
+        // B rows this wave may read past wrow: plain, local rows bw0 ..
+        // rows_b - 1; SWIGLU, the 64 rows of its half (all valid)
+        const uint32_t nbr = SWIGLU ? 64u : (uint32_t)max(0, rows_b - bw0);
+        dA = make_desc_n(uniform_ptr(p.a_codes + m_base * (int64_t)KB), (uint32_t)rows_a * KB);
+        dB = make_desc_n(uniform_ptr(p.w_codes + wrow * (int64_t)KB), nbr * KB);
+        dAs = make_desc_n(uniform_ptr(p.a_bscale + m_base * (int64_t)KS), (uint32_t)rows_a * KS);
+        dBs = make_desc_n(uniform_ptr(p.w_bscale + wrow * (int64_t)KS), nbr * KS);
+        // column scales in natural order: rs_w[c] is output column c of the
+        // tile (SWIGLU: gate rows at 0..127, up rows at 128..255)
+        rs_w_src = SWIGLU ? uniform_ptr(p.w_rscale + (int64_t)e * p.N + 128 * (int64_t)nt + (wave >= 2 ? p.N / 2 - 128 : 0))
+                          : uniform_ptr(p.w_rscale + (int64_t)e * p.N + n_base);
+    };
+
+    // DMA of super-stage S into ring slot q in 12 parts of 2
+    // instructions: parts 0..7 code rows (A and B of instruction i),
+    // parts 8..11 scale rows.  Chunks past K read as zero.
+    auto issue_part = [&](int S, uint32_t q, int part, bool ok) {
+        // Offsets are summed here from laundered bases, so the compiler adds
+        // them at the DMA rather than keeping one live register per
+        // (instruction, operand) across the loops.
+        if (part < 8) {
+            const int i = part;
+            // B: ring position 64 w + 8 i + lane / 8 holds local row bw0 + 4 (lane / 8) + bir
+            // (SWIGLU: 2 (lane / 8))
+            const int bir = SWIGLU ? 16 * (i & 3) + (i >> 2) : 32 * (i & 3) + (i >> 2);
+            const uint32_t kb = opaque_s(KB);
+            const uint32_t ks = (uint32_t)S * FS_CB;
+            const uint32_t vch = (i & 1) ? vch1 : vch0;
+            const bool okk = ok & (ks + vch < KB);  // chunk inside the row (K tail)
+            const uint32_t ldst = q * FS_CODE_TILE + 1024u * (uint32_t)(8 * wave + i);
+            const uint32_t oa = opaque_v(vra) + vch + (ks + (uint32_t)(8 * i) * kb);
+            const uint32_t ob = opaque_v(vrb) + vch + (ks + (uint32_t)bir * kb);
+            dma16(dA, okk ? oa : OOB, LA + ldst);
+            dma16(dB, okk ? ob : OOB, LB + ldst);
+        } else {
+            const int i = part - 8;
+            // B: ring position 64 w + 16 i + lane / 4 holds local row bw0 + 4 (lane / 4) + sir
+            // (SWIGLU: 2 (lane / 4))
+            const int sir = SWIGLU ? 32 * (i & 1) + (i >> 1) : 64 * (i & 1) + (i >> 1);
+            const uint32_t kq = opaque_s(KS);
+            const uint32_t so = (uint32_t)S * FS_SB;
+            const bool oks = ok & (so + 4 * sdw < KS);
+            const uint32_t ldst = q * FS_SCALE_TILE + 256u * (uint32_t)(4 * wave + i);
+            const uint32_t oa = opaque_v(vsa) + (so + (uint32_t)(16 * i) * kq);
+            const uint32_t ob = opaque_v(vsb) + (so + (uint32_t)sir * kq);
+            dma4(dAs, oks ? oa : OOB, LSA + ldst);
+            dma4(dBs, oks ? ob : OOB, LSB + ldst);
+        }
+    };
+    // the tile's row and column scales into buffer rb
+    auto issue_rscale = [&](int rb) {
+        const int r = 64 * wave + lane;
+        dma4(make_desc(uniform_ptr(p.a_rscale + m_base)), r < rows_a ? 4u * (uint32_t)r : OOB,
+             LRA + 1024u * (uint32_t)rb + 256u * wave);
+        dma4(make_desc(rs_w_src), r < rows_b ? 4u * (uint32_t)r : OOB, LRW + 1024u * (uint32_t)rb + 256u * wave);
+    };
+
+    // LDS reads of group G (super-stage G / 4, group G % 4 of it); part f
+    // (0..7) reads fragment f: A rows of group f, or B rows of group f - 4.
+    auto read_part = [&](int G, FwdRaw& r, int f) {
+        const uint32_t q = (((uint32_t)G >> 2) + par) & 1, gg = (uint32_t)G & 3;
+        const int i = f & 3;
+        const uint32_t co = ((f < 4) ? fa : fb) + q * FS_CODE_TILE + (uint32_t)(32 * i * FS_CB);
+        const uint32_t so = ((f < 4) ? fsa : fsb) + q * FS_SCALE_TILE + (uint32_t)(32 * i * FS_SB) + 4 * gg;
+        r.c[f] = *(const __attribute__((address_space(3))) u32x4*)(lds + co + (fr ^ (32u * gg)));
+        r.s[f] = *(const __attribute__((address_space(3))) uint32_t*)(lds + so);
+    };
+    // this lane's two block scales of fragment f in the group, as fp16
+    auto conv_scale = [&](const FwdRaw& r, int f) -> half2v {
+        return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.s[f] >> (16 * g), 1.0f, false);
+    };
+
+    // Tile pipeline.  A tile's super-stage 0 lives in ring slot `par`.  The
+    // refill slot of super-stage S always fills the slot S just released:
+    // with super-stage S + 2 of this tile while there is one, then with
+    // super-stages 0 and 1 of the next tile (whose DMA state setup() loads
+    // at the start of super-stage nsup - 2, when this tile's DMA is all
+    // issued), else with nothing (out-of-range reads).  The schedule thus
+    // has no branches, and the next tile's operands land under this tile's
+    // MFMAs.  Tiles with fewer than 3 super-stages start the next tile's DMA
+    // after the main loop.
+    if (tile >= 0) {
+        setup(tile);
+#pragma unroll
+        for (int part = 0; part < 12; ++part) issue_part(0, 0, part, true);
+#pragma unroll
+        for (int part = 0; part < 12; ++part) issue_part(1, 1, part, true);
+        issue_rscale(0);
+        wait_vmcnt<0>();
+    }
+
     for (;;) {
         if (tile < 0) break;
         // claim the next tile now; the atomic's latency hides behind this one
         int next_tile = 0;
         if (tid == 0) next_tile = claim_tile(p.plan, xcd, total, dq);
-
-        const TileRef tr = decode_tile_any(tab_lds, tab, p.plan, p.offsets, p.E, tile, lane);
-        const int e = tr.e;
-        const int local = tr.local;
-        const int64_t off0 = tr.off0;
-        const int64_t off1 = tr.off1;
-        int mt, nt;
-        grouped_tile(local, (int)((off1 - off0 + FWD_BM - 1) / FWD_BM), NT, mt, nt);
-        const int64_t m_base = uniform_i64(off0 + (int64_t)mt * FWD_BM);
-        const int rows_a = __builtin_amdgcn_readfirstlane((int)min((int64_t)FWD_BM, off1 - m_base));
-        const int64_t n_base = uniform_i64((int64_t)nt * FWD_BN);
-        // first weight row of this wave's B rows (SWIGLU: waves 2-3 take the up half)
-        const int64_t wrow = SWIGLU ? uniform_i64((int64_t)e * p.N + 128 * (int64_t)nt + (wave >= 2 ? p.N / 2 - 128 : 0))
-                                    : uniform_i64((int64_t)e * p.N + n_base);
-        const int rows_b = SWIGLU ? FWD_BN : __builtin_amdgcn_readfirstlane((int)min((int64_t)FWD_BN, p.N - n_base));
-        const i32x4 dA = make_desc(uniform_ptr(p.a_codes + m_base * (int64_t)KB));
-        const i32x4 dB = make_desc(uniform_ptr(p.w_codes + wrow * (int64_t)KB));
-        const i32x4 dAs = make_desc(uniform_ptr(p.a_bscale + m_base * (int64_t)KS));
-        const i32x4 dBs = make_desc(uniform_ptr(p.w_bscale + wrow * (int64_t)KS));
-
-        const uint32_t vra = (uint32_t)drow0 * KB, vrb = (uint32_t)drow0 * KB;
-        const uint32_t vsa = (uint32_t)srow0 * KS + 4 * sdw, vsb = vsa;
-
-        // DMA of super-stage S into ring slot S % 2 in 12 parts of 2
-        // instructions: parts 0..7 code rows (A and B of instruction i),
-        // parts 8..11 scale rows.  Chunks past K read as zero.
-        auto issue_part = [&](int S, int part) {
-            const uint32_t q = (uint32_t)S & 1;
-            if (part < 8) {
-                const int i = part;
-                const int row = drow0 + 8 * i;
-                const uint32_t ko = (uint32_t)S * FS_CB + 16 * ((i & 1) ? dch1 : dch0);
-                const bool okk = ko < KB;
-                const uint32_t ldst = q * FS_CODE_TILE + 1024u * (uint32_t)(8 * wave + i);
-                dma16(dA, (okk & (row < rows_a)) ? vra + (uint32_t)(8 * i) * KB + ko : OOB, LA + ldst);
-                dma16(dB, (okk & (row < rows_b)) ? vrb + (uint32_t)(8 * i) * KB + ko : OOB, LB + ldst);
-            } else {
-                const int i = part - 8;
-                const int row = srow0 + 16 * i;
-                const uint32_t so = (uint32_t)S * FS_SB;
-                const bool oks = so + 4 * sdw < KS;
-                const uint32_t ldst = q * FS_SCALE_TILE + 256u * (uint32_t)(4 * wave + i);
-                dma4(dAs, (oks & (row < rows_a)) ? vsa + (uint32_t)(16 * i) * KS + so : OOB, LSA + ldst);
-                dma4(dBs, (oks & (row < rows_b)) ? vsb + (uint32_t)(16 * i) * KS + so : OOB, LSB + ldst);
-            }
-        };
-        // LDS reads of group G (super-stage G / 4, group G % 4 of it); part f
-        // (0..7) reads fragment f: A rows of group f, or B rows of group f - 4.
-        auto read_part = [&](int G, FwdRaw& r, int f) {
-            const uint32_t q = ((uint32_t)G >> 2) & 1, gg = (uint32_t)G & 3;
-            const int i = f & 3;
-            const uint32_t co = ((f < 4) ? fa : fb) + q * FS_CODE_TILE + (uint32_t)(32 * i * FS_CB);
-            const uint32_t so = ((f < 4) ? fsa : fsb) + q * FS_SCALE_TILE + (uint32_t)(32 * i * FS_SB) + 4 * gg;
-            r.c[f] = *(const __attribute__((address_space(3))) u32x4*)(lds + co + (fr ^ (32u * gg)));
-            r.s[f] = *(const __attribute__((address_space(3))) uint32_t*)(lds + so);
-        };
-        // this lane's two block scales of fragment f in the group, as fp16
-        auto conv_scale = [&](const FwdRaw& r, int f) -> half2v {
-            return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.s[f] >> (16 * g), 1.0f, false);
-        };
+        // this tile's epilogue coordinates (setup() moves on to the next tile
+        // during the last super-stage)
+        const int64_t em = m_base, en = n_base;
+        const int ea = rows_a, eb = rows_b, ent = nt, erb = rb;
+        const uint32_t qn = ((uint32_t)nsup + par) & 1;  // slot of the next tile's super-stage 0
+        int ntile = -1;
+        bool has_next = false;  // the DMA state holds the next tile's
 
         float16v acc[4][4];
 #pragma unroll
@@ -233,17 +329,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-        // Prologue: the tile's row and column scales, super-stages 0 and 1.
-        {
-            const int r = 64 * wave + lane;
-            dma4(make_desc(uniform_ptr(p.a_rscale + m_base)), r < rows_a ? 4u * (uint32_t)r : OOB, LRA + 256u * wave);
-            dma4(make_desc(uniform_ptr(p.w_rscale + wrow)), r < rows_b ? 4u * (uint32_t)r : OOB, LRW + 256u * wave);
-        }
-#pragma unroll
-        for (int part = 0; part < 12; ++part) issue_part(0, part);
-#pragma unroll
-        for (int part = 0; part < 12; ++part) issue_part(1, part);
-        wait_vmcnt<FS_DMA>();
+        // every wave waited for its own share of super-stages 0 and 1 (and
+        // the scales) after its previous epilogue
         block_barrier();
 
         FwdRaw raw[2];
@@ -272,8 +359,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
                     const FwdOps& o = ops[j & 1];
                     FwdOps& on = ops[(j + 1) & 1];
                     if (j == 0 && gg == 3) {
-                        // super-stage S+1 has landed (the only DMA in flight)
-                        // and every wave is done reading slot S % 2
+                        // the DMA issued one super-stage ago (super-stage
+                        // S+1, or the next tile's 0) has landed, and every
+                        // wave is done reading this slot
                         wait_vmcnt<0>();
                         wait_lgkmcnt0();
                         block_barrier();
@@ -295,129 +383,132 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
                         // LDS reads of the next group
                         if (j == 0 && k < 8) read_part(G + 1, nxt, k);
                         // refill of the slot just freed with super-stage S+2
-                        if (gg == 3 && j == 1 && k < 12 && S + 2 < nsup) issue_part(S + 2, k);
+                        // (this tile's super-stage S+2, else the next tile's S+2-nsup)
+                        if (gg == 3 && j == 1 && k < 12)
+                            issue_part(S + 2 < nsup ? S + 2 : S + 2 - nsup, ((uint32_t)S + par) & 1, k,
+                                       (S + 2 < nsup) | has_next);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
         };
-        for (int S = 0; S < nsup; ++S) superstage(S);
-
-        // drain every DMA of this tile before the ring is reused
-        wait_vmcnt<0>();
-        wait_lgkmcnt0();
-        block_barrier();
-
-        // Epilogue: the fp32 tile goes through the idle ring in two passes of
-        // 128 rows, scaled by s_a[row] and then s_w[col] when it leaves as
-        // whole rows in 16-byte stores (bf16 rounded to nearest even).  Lane
-        // (lr, g) holds column wn*128 + 32j + lr of rows
-        // wm*128 + 32i + 8(v/4) + 4g + v%4; the staging pitch of 1056 bytes
-        // puts the two lane halves on disjoint banks.
-        {
-            constexpr uint32_t EP = 1056;
-            // SWIGLU: the tile's H columns start at 128 nt of rows of p.ldo elements
-            const __amdgpu_buffer_rsrc_t rc =
-                make_rsrc(uniform_ptr(reinterpret_cast<char*>(p.y) +
-                                      (SWIGLU ? (m_base * p.ldo + 128 * (int64_t)nt) * 2 : (m_base * p.N + n_base) * esz)),
-                          0x7FFFFFFFu);
-            const uint32_t ldcb = SWIGLU ? (uint32_t)p.ldo * 2u : (uint32_t)p.N * (uint32_t)esz;
-            __attribute__((address_space(3))) uint8_t* st = (__attribute__((address_space(3))) uint8_t*)(smem_raw);
-            const __attribute__((address_space(3))) float* rsa =
-                (const __attribute__((address_space(3))) float*)(st + offsetof(FwdSmem, rs_a));
-            const __attribute__((address_space(3))) float* rsw =
-                (const __attribute__((address_space(3))) float*)(st + offsetof(FwdSmem, rs_w));
-            const uint32_t wbase = (uint32_t)(wm * 64 + 4 * g) * EP + (uint32_t)(wn * 128 + lr) * 4u;
-#pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int i = 2 * pass + ii;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const uint32_t o = wbase + (uint32_t)(32 * ii + 8 * (v >> 2) + (v & 3)) * EP + 128u * j;
-                            *(__attribute__((address_space(3))) float*)(st + o) = acc[i][j][v];
-                        }
-                }
-                wait_lgkmcnt0();
-                block_barrier();
-                // staged row r (0..127) is tile row (r / 64) * 128 + 64 * pass + r % 64
-                if constexpr (SWIGLU) {
-#pragma unroll 2
-                    for (int it = 0; it < 8; ++it) {
-                        const int c = it * 256 + tid;  // 16 chunks of 8 H columns per row
-                        const int r = c >> 4, cc = c & 15;
-                        const int row = (r >> 6) * 128 + 64 * pass + (r & 63);
-                        const uint32_t ro = (uint32_t)r * EP + 32u * cc;
-                        const u32x4 g0 = *(const __attribute__((address_space(3))) u32x4*)(st + ro);
-                        const u32x4 g1 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + 16u);
-                        const u32x4 u0 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + 512u);
-                        const u32x4 u1 = *(const __attribute__((address_space(3))) u32x4*)(st + ro + 528u);
-                        const float sa = rsa[row];
-                        float gv[8], uv[8];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            gv[q] = (__uint_as_float(g0[q]) * sa) * rsw[8 * cc + q];
-                            gv[4 + q] = (__uint_as_float(g1[q]) * sa) * rsw[8 * cc + 4 + q];
-                            uv[q] = (__uint_as_float(u0[q]) * sa) * rsw[128 + 8 * cc + q];
-                            uv[4 + q] = (__uint_as_float(u1[q]) * sa) * rsw[128 + 8 * cc + 4 + q];
-                        }
-                        u32x4 y;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            y[q] = swiglu_pair(pack_bf16x2(gv[2 * q], gv[2 * q + 1]), pack_bf16x2(uv[2 * q], uv[2 * q + 1]));
-                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, row < rows_a ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB,
-                                                               0, OUT_STORE_NT);
-                    }
-                } else if constexpr (OUT_F32) {
-#pragma unroll 4
-                    for (int it = 0; it < 32; ++it) {
-                        const int c = it * 256 + tid;  // 64 chunks of 4 columns per row
-                        const int r = c >> 6, cc = c & 63;
-                        const int row = (r >> 6) * 128 + 64 * pass + (r & 63);
-                        const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 16u * cc);
-                        const float sa = rsa[row];
-                        u32x4 y;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) y[q] = __float_as_uint((__uint_as_float(x[q]) * sa) * rsw[4 * cc + q]);
-                        const bool ok = (row < rows_a) & (4 * cc < rows_b);
-                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0,
-                                                               OUT_STORE_NT);
-                    }
-                } else {
-#pragma unroll 4
-                    for (int it = 0; it < 16; ++it) {
-                        const int c = it * 256 + tid;  // 32 chunks of 8 columns per row
-                        const int r = c >> 5, cc = c & 31;
-                        const int row = (r >> 6) * 128 + 64 * pass + (r & 63);
-                        const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 32u * cc);
-                        const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(st + (uint32_t)r * EP + 32u * cc + 16u);
-                        const float sa = rsa[row];
-                        float v[8];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            v[q] = (__uint_as_float(x0[q]) * sa) * rsw[8 * cc + q];
-                            v[4 + q] = (__uint_as_float(x1[q]) * sa) * rsw[8 * cc + 4 + q];
-                        }
-                        u32x4 y;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) y[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
-                        const bool ok = (row < rows_a) & (8 * cc < rows_b);
-                        __builtin_amdgcn_raw_buffer_store_b128(y, rc, ok ? (int)((uint32_t)row * ldcb + 16u * cc) : (int)OOB, 0,
-                                                               OUT_STORE_NT);
+        for (int S = 0; S < nsup; ++S) {
+            // the barrier inside super-stage nsup - 3 publishes the next
+            // tile; from super-stage nsup - 2 on the DMA state is the next
+            // tile's
+            if (nsup >= 3) {
+                if (S == nsup - 3 && tid == 0) s_tile = next_tile;
+                if (S == nsup - 2) {
+                    ntile = __builtin_amdgcn_readfirstlane(s_tile);
+                    has_next = ntile >= 0;
+                    if (has_next) {
+                        setup(ntile);
+                        issue_rscale(rb ^ 1);
                     }
                 }
-                // every wave's reads of this pass are done before the next
-                // pass (or the next tile's DMA) overwrites the staging area;
-                // the last barrier also publishes the next tile
-                if (pass == 1 && tid == 0) s_tile = next_tile;
-                wait_lgkmcnt0();
-                block_barrier();
+            }
+            superstage(S);
+        }
+
+        if (nsup < 3) {
+            // every wave is done with the ring; the next tile's DMA now
+            wait_lgkmcnt0();
+            if (tid == 0) s_tile = next_tile;
+            block_barrier();
+            ntile = __builtin_amdgcn_readfirstlane(s_tile);
+            if (ntile >= 0) {
+                setup(ntile);
+#pragma unroll
+                for (int part = 0; part < 12; ++part) issue_part(0, qn, part, true);
+#pragma unroll
+                for (int part = 0; part < 12; ++part) issue_part(1, qn ^ 1u, part, true);
+                issue_rscale(rb ^ 1);
             }
         }
-        tile = __builtin_amdgcn_readfirstlane(s_tile);
+
+        // Epilogue straight from the accumulators.  Lane (lr, g) of wave
+        // (wm, wn) holds, in acc[i][j][v], tile row wm*128 + 32i + 8(v/4) +
+        // 4g + v%4 and ring column position 128 wn + 32 j + lr.  Each value is
+        // scaled by s_a[row] and then s_w[col] and rounded once (bf16 to
+        // nearest even); rows past the expert's end and columns past N are not
+        // stored.  A store instruction writes two rows of 256 contiguous bytes
+        // (plain bf16; 512 for fp32; SWIGLU: 128 bytes of H).
+        {
+            const __attribute__((address_space(3))) float* rsa =
+                (const __attribute__((address_space(3))) float*)(lds + offsetof(FwdSmem, rs_a) + 1024u * (uint32_t)erb);
+            const __attribute__((address_space(3))) float* rsw =
+                (const __attribute__((address_space(3))) float*)(lds + offsetof(FwdSmem, rs_w) + 1024u * (uint32_t)erb);
+            const __amdgpu_buffer_rsrc_t rc =
+                make_rsrc(uniform_ptr(reinterpret_cast<char*>(p.y) +
+                                      (SWIGLU ? (em * p.ldo + 128 * (int64_t)ent) * 2 : (em * p.N + en) * esz)),
+                          0x7FFFFFFFu);
+            // laundered: the row offsets and LDS addresses below are the same
+            // for every tile, and hoisting them would keep 80 registers live
+            // across the main loop
+            const uint32_t ldcb = opaque_s(SWIGLU ? (uint32_t)p.ldo * 2u : (uint32_t)p.N * (uint32_t)esz);
+            const int r0w = (int)opaque_v((uint32_t)(wm * 128 + 4 * g));
+            if constexpr (SWIGLU) {
+                const int c = 64 * wn + 2 * lr;  // H columns c, c + 1 of the tile
+                const f32x2 swg = *(const __attribute__((address_space(3))) f32x2*)(rsw + c);
+                const f32x2 swu = *(const __attribute__((address_space(3))) f32x2*)(rsw + 128 + c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int vq = 0; vq < 4; ++vq) {
+                        const int r0 = r0w + 32 * i + 8 * vq;
+                        const f32x4 sa4 = *(const __attribute__((address_space(3))) f32x4*)(rsa + r0);
+#pragma unroll
+                        for (int vv = 0; vv < 4; ++vv) {
+                            const int v = 4 * vq + vv;
+                            const float sa = sa4[vv];
+                            const float g0 = (acc[i][0][v] * sa) * swg[0], g1 = (acc[i][1][v] * sa) * swg[1];
+                            const float u0 = (acc[i][2][v] * sa) * swu[0], u1 = (acc[i][3][v] * sa) * swu[1];
+                            const uint32_t hv = swiglu_pair(pack_bf16x2(g0, g1), pack_bf16x2(u0, u1));
+                            const int row = r0 + vv;
+                            __builtin_amdgcn_raw_buffer_store_b32(hv, rc, row < ea ? (int)((uint32_t)row * ldcb + 2u * (uint32_t)c) : (int)OOB,
+                                                                  0, OUT_STORE_NT);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            } else {
+                const int col = wn * 128 + 4 * lr;  // columns col .. col + 3 of the tile
+                const bool okc = col < eb;
+                const f32x4 sw = *(const __attribute__((address_space(3))) f32x4*)(rsw + col);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int vq = 0; vq < 4; ++vq) {
+                        const int r0 = r0w + 32 * i + 8 * vq;
+                        const f32x4 sa4 = *(const __attribute__((address_space(3))) f32x4*)(rsa + r0);
+#pragma unroll
+                        for (int vv = 0; vv < 4; ++vv) {
+                            const int v = 4 * vq + vv;
+                            const float sa = sa4[vv];
+                            const float y0 = (acc[i][0][v] * sa) * sw[0], y1 = (acc[i][1][v] * sa) * sw[1];
+                            const float y2 = (acc[i][2][v] * sa) * sw[2], y3 = (acc[i][3][v] * sa) * sw[3];
+                            const int row = r0 + vv;
+                            const int off = (okc & (row < ea)) ? (int)((uint32_t)row * ldcb + (uint32_t)(col * esz)) : (int)OOB;
+                            if constexpr (OUT_F32) {
+                                u32x4 y;
+                                y[0] = __float_as_uint(y0); y[1] = __float_as_uint(y1);
+                                y[2] = __float_as_uint(y2); y[3] = __float_as_uint(y3);
+                                __builtin_amdgcn_raw_buffer_store_b128(y, rc, off, 0, OUT_STORE_NT);
+                            } else {
+                                u32x2 y;
+                                y[0] = pack_bf16x2(y0, y1);
+                                y[1] = pack_bf16x2(y2, y3);
+                                __builtin_amdgcn_raw_buffer_store_b64(y, rc, off, 0, OUT_STORE_NT);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
+        }
+        // the next tile's super-stages 0 and 1 and scales (and these stores)
+        wait_vmcnt<0>();
+        par = qn;
+        rb ^= 1;
+        tile = ntile;
     }
 }
 

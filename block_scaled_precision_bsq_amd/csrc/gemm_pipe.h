@@ -57,6 +57,25 @@ __device__ __forceinline__ i32x4 make_desc(const void* base) {
     return r;
 }
 
+// Descriptor whose byte range ends at `bytes`: offsets at or past it read as
+// zero (the row limit of a partial tile).
+__device__ __forceinline__ i32x4 make_desc_n(const void* base, uint32_t bytes) {
+    i32x4 r = make_desc(base);
+    r.z = (int)bytes;
+    return r;
+}
+
+// Values laundered through an empty asm: the compiler can no longer see them
+// as loop invariants, so sums built from them are formed at their use.
+__device__ __forceinline__ uint32_t opaque_v(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ uint32_t opaque_s(uint32_t x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
