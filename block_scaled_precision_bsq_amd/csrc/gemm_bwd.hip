@@ -59,8 +59,7 @@ constexpr int SS_TILE = PIPE_ROWS * SS_BK;       // one operand's super-stage (3
 
 // One ring slot: codes of both operands and their scale bytes (one dword per
 // (k block, row): block * 256 + row).  Slot-major so that a whole slot is
-// one contiguous region -- the epilogue stages its output through slot 1
-// while the next tile's first super-stage lands in slot 0.
+// one contiguous region: the epilogue stages its output through slot 1.
 struct BwdSlot {
     uint8_t a[SS_TILE];
     uint8_t b[SS_TILE];
@@ -196,7 +195,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_ws(BwdArgs p) {
     const int xcd = blockIdx.x & 7;
     constexpr int esz = OUT_F32 ? 4 : 2;
     const int total = p.plan[PLAN_TOTAL];
-    int dq = 0;
+    int qdone = 0;  // claim queues found drained
 
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem_raw));
     const __attribute__((address_space(3))) uint8_t* lds =
@@ -205,7 +204,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_ws(BwdArgs p) {
         (__attribute__((address_space(3))) int32_t*)(smem_raw + sizeof(BwdSmem));
     const bool tab_lds = p.E <= LDS_TABLE_MAX_E;
     if (tab_lds) fill_lds_tables(tab, p.plan, p.offsets, p.E);
-    if (tid0 == 0) s_tile = claim_tile(p.plan, xcd, total, dq);
+    if (tid0 == 0) s_tile = claim_tile(p.plan, xcd, total, qdone);
     __syncthreads();
     int tile = __builtin_amdgcn_readfirstlane(s_tile);
     if (tile < 0) return;
@@ -420,8 +419,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_ws(BwdArgs p) {
         const uint32_t fsa = offsetof(BwdSlot, sa) + ESA * (uint32_t)(256 * g + wm * 128 + lr);
         const uint32_t fsb = offsetof(BwdSlot, sb) + (uint32_t)(256 * g + wn * 64 + lr);
 
-        int next_tile = 0;
-        if (tid == 0) next_tile = claim_tile(p.plan, xcd, total, dq);
+        // the next tile's claim: its atomic's round trip overlaps this tile
+        PendingClaim pclaim{0, -1};
+        if (tid == 0) pclaim = claim_start(p.plan, xcd, qdone);
 
         // Fragments of k step t: row group grp (32 rows) of A (isB false) or
         // B, logical chunks 4h + g and 4h + g + 2 of the row, and the scale of
@@ -582,13 +582,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_ws(BwdArgs p) {
         else
             kloop(IC<0>{});
         if (dwave) wait_vmcnt<0>();
-        if (tid == 0) s_tile = next_tile;
+        if (tid == 0) s_tile = claim_finish(p.plan, xcd, total, qdone, pclaim);
         wait_lgkmcnt0();
         block_barrier();
         tile = __builtin_amdgcn_readfirstlane(s_tile);
 
         const int tnext = tile >= 0 ? tile : 0;
-        if (dwave && tile >= 0) issue(setup(tnext), 0);
 
         {
             const __amdgpu_buffer_rsrc_t rc = make_rsrc(cur.c, 0x7FFFFFFFu);
@@ -697,7 +696,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bwd_ws(BwdArgs p) {
             }
         }
         if (tile < 0) break;
-        if (dwave) issue(setup(tnext), 1);
+        // The next tile's first two super-stages go out only now: issued
+        // before the epilogue, their loads sat in the CU's memory queue ahead
+        // of the output stores and held the epilogue up.
+        if (dwave) {
+            const BwdTile nx = setup(tnext);
+            issue(nx, 0);
+            issue(nx, 1);
+        }
     }
 }
 

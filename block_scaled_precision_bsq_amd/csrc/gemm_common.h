@@ -58,6 +58,31 @@ __device__ __forceinline__ int claim_tile(int32_t* plan, int xcd, int total, int
     return -1;
 }
 
+// The same claim in two halves, so that the atomic's round trip overlaps a
+// tile's work: claim_start issues the first attempt (the counter value
+// comes back in the background; nothing waits for it until it is used) and
+// claim_finish decodes it, falling back to claim_tile when that queue was
+// already drained.  Thread 0 only.
+struct PendingClaim {
+    int c;  // counter value returned by the atomic
+    int q;  // queue it came from; -1 when every queue was already empty
+};
+__device__ __forceinline__ PendingClaim claim_start(int32_t* plan, int xcd, int d) {
+    PendingClaim r{0, -1};
+    if (d < 8) {
+        r.q = (xcd + d) & 7;
+        r.c = atomicAdd(&plan[PLAN_CTR + r.q], 1);
+    }
+    return r;
+}
+__device__ __forceinline__ int claim_finish(int32_t* plan, int xcd, int total, int& d, PendingClaim pc) {
+    if (pc.q < 0) return -1;
+    const int t = (pc.q + 8 * (pc.c / XCD_CHUNK)) * XCD_CHUNK + (pc.c % XCD_CHUNK);
+    if (t < total) return t;
+    ++d;
+    return claim_tile(plan, xcd, total, d);
+}
+
 // Grouped order inside one expert: local index -> (row-tile, column-tile).
 // GROUP_M row-tiles are swept together across all `nt` column-tiles.
 __device__ __forceinline__ void grouped_tile(int local, int mt_count, int nt, int& mt, int& ct) {

@@ -310,9 +310,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
 
     for (;;) {
         if (tile < 0) break;
-        // claim the next tile now; the atomic's latency hides behind this one
-        int next_tile = 0;
-        if (tid == 0) next_tile = claim_tile(p.plan, xcd, total, dq);
+        // claim the next tile now; the atomic's round trip hides behind
+        // this tile (its value is first read when the next tile is published)
+        PendingClaim pclaim{0, -1};
+        if (tid == 0) pclaim = claim_start(p.plan, xcd, dq);
         // this tile's epilogue coordinates (setup() moves on to the next tile
         // during the last super-stage)
         const int64_t em = m_base, en = n_base;
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
             // tile; from super-stage nsup - 2 on the DMA state is the next
             // tile's
             if (nsup >= 3) {
-                if (S == nsup - 3 && tid == 0) s_tile = next_tile;
+                if (S == nsup - 3 && tid == 0) s_tile = claim_finish(p.plan, xcd, total, dq, pclaim);
                 if (S == nsup - 2) {
                     ntile = __builtin_amdgcn_readfirstlane(s_tile);
                     has_next = ntile >= 0;
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
         if (nsup < 3) {
             // every wave is done with the ring; the next tile's DMA now
             wait_lgkmcnt0();
-            if (tid == 0) s_tile = next_tile;
+            if (tid == 0) s_tile = claim_finish(p.plan, xcd, total, dq, pclaim);
             block_barrier();
             ntile = __builtin_amdgcn_readfirstlane(s_tile);
             if (ntile >= 0) {
