@@ -166,8 +166,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     const uint32_t fr = (uint32_t)(lr * FS_CB + 16 * (g ^ swz8(lr)));
     const uint32_t fa = offsetof(FwdSmem, a) + (uint32_t)(wm * 128 * FS_CB);
     const uint32_t fb = offsetof(FwdSmem, b) + (uint32_t)(wn * 128 * FS_CB);
-    const uint32_t fsa = offsetof(FwdSmem, sa) + (uint32_t)((wm * 128 + lr) * FS_SB);
-    const uint32_t fsb = offsetof(FwdSmem, sb) + (uint32_t)((wn * 128 + lr) * FS_SB);
+    // (lane group g's two scale bytes of a group sit at byte 2g of its dword)
+    const uint32_t fsa = offsetof(FwdSmem, sa) + (uint32_t)((wm * 128 + lr) * FS_SB + 2 * g);
+    const uint32_t fsb = offsetof(FwdSmem, sb) + (uint32_t)((wn * 128 + lr) * FS_SB + 2 * g);
 
     // decode tables in LDS behind the staging buffers (when they fit)
     __attribute__((address_space(3))) int32_t* tab =
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     // term (see issue_part).
     int64_t m_base = 0, n_base = 0;
     int rows_a = 0, rows_b = 0, nt = 0;
-    i32x4 dA = {}, dB = {}, dAs = {}, dBs = {};
+    __amdgpu_buffer_rsrc_t dA = rsrc_n(nullptr, 0), dB = dA, dAs = dA, dBs = dA;
     const float* rs_w_src = nullptr;
     const int bw0 = SWIGLU ? 64 * (wave >> 1) : 128 * (wave >> 1) + 2 * (wave & 1);  // local B row, wave term
     // Per-lane DMA offsets at k = 0 (codes: row part only, the chunk comes
@@ -201,6 +202,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     const uint32_t vsa = (uint32_t)srow0 * KS + 4 * sdw;
     const uint32_t vsb = (uint32_t)((SWIGLU ? 2 : 4) * (lane >> 2)) * KS + 4 * sdw;
     const uint32_t vch0 = 16 * dch0, vch1 = 16 * dch1;
+    // with the chunk of each parity folded in (instruction i uses parity i & 1)
+    const uint32_t va0 = vra + vch0, va1 = vra + vch1, vb0 = vrb + vch0, vb1 = vrb + vch1;
 
     uint32_t par = 0;  // ring slot of the current tile's super-stage 0
     int rb = 0;        // scale buffer of the current tile
@@ -220,10 +223,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
         // B rows this wave may read past wrow: plain, local rows bw0 ..
         // rows_b - 1; SWIGLU, the 64 rows of its half (all valid)
         const uint32_t nbr = SWIGLU ? 64u : (uint32_t)max(0, rows_b - bw0);
-        dA = make_desc_n(uniform_ptr(p.a_codes + m_base * (int64_t)KB), (uint32_t)rows_a * KB);
-        dB = make_desc_n(uniform_ptr(p.w_codes + wrow * (int64_t)KB), nbr * KB);
-        dAs = make_desc_n(uniform_ptr(p.a_bscale + m_base * (int64_t)KS), (uint32_t)rows_a * KS);
-        dBs = make_desc_n(uniform_ptr(p.w_bscale + wrow * (int64_t)KS), nbr * KS);
+        dA = rsrc_n(uniform_ptr(p.a_codes + m_base * (int64_t)KB), (uint32_t)rows_a * KB);
+        dB = rsrc_n(uniform_ptr(p.w_codes + wrow * (int64_t)KB), nbr * KB);
+        dAs = rsrc_n(uniform_ptr(p.a_bscale + m_base * (int64_t)KS), (uint32_t)rows_a * KS);
+        dBs = rsrc_n(uniform_ptr(p.w_bscale + wrow * (int64_t)KS), nbr * KS);
         // column scales in natural order: rs_w[c] is output column c of the
         // tile (SWIGLU: gate rows at 0..127, up rows at 128..255)
         rs_w_src = SWIGLU ? uniform_ptr(p.w_rscale + (int64_t)e * p.N + 128 * (int64_t)nt + (wave >= 2 ? p.N / 2 - 128 : 0))
@@ -234,8 +237,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     // instructions: parts 0..7 code rows (A and B of instruction i),
     // parts 8..11 scale rows.  Chunks past K read as zero.
     auto issue_part = [&](int S, uint32_t q, int part, bool ok) {
-        // Offsets are summed here from laundered bases, so the compiler adds
-        // them at the DMA rather than keeping one live register per
+        // Each offset is a loop-invariant lane base plus a wave-uniform term;
+        // the row pitch is laundered at each use, so the compiler forms the
+        // sum at the DMA instead of keeping one live register per
         // (instruction, operand) across the loops.
         if (part < 8) {
             const int i = part;
@@ -244,13 +248,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
             const int bir = SWIGLU ? 16 * (i & 3) + (i >> 2) : 32 * (i & 3) + (i >> 2);
             const uint32_t kb = opaque_s(KB);
             const uint32_t ks = (uint32_t)S * FS_CB;
-            const uint32_t vch = (i & 1) ? vch1 : vch0;
-            const bool okk = ok & (ks + vch < KB);  // chunk inside the row (K tail)
+            const bool okk = ok & (ks + ((i & 1) ? vch1 : vch0) < KB);  // chunk inside the row (K tail)
             const uint32_t ldst = q * FS_CODE_TILE + 1024u * (uint32_t)(8 * wave + i);
-            const uint32_t oa = opaque_v(vra) + vch + (ks + (uint32_t)(8 * i) * kb);
-            const uint32_t ob = opaque_v(vrb) + vch + (ks + (uint32_t)bir * kb);
-            dma16(dA, okk ? oa : OOB, LA + ldst);
-            dma16(dB, okk ? ob : OOB, LB + ldst);
+            const uint32_t oa = ((i & 1) ? va1 : va0) + (ks + (uint32_t)(8 * i) * kb);
+            const uint32_t ob = ((i & 1) ? vb1 : vb0) + (ks + (uint32_t)bir * kb);
+            dma_lds_r<16>(dA, okk ? oa : OOB, LA + ldst);
+            dma_lds_r<16>(dB, okk ? ob : OOB, LB + ldst);
         } else {
             const int i = part - 8;
             // B: ring position 64 w + 16 i + lane / 4 holds local row bw0 + 4 (lane / 4) + sir
@@ -260,10 +263,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
             const uint32_t so = (uint32_t)S * FS_SB;
             const bool oks = ok & (so + 4 * sdw < KS);
             const uint32_t ldst = q * FS_SCALE_TILE + 256u * (uint32_t)(4 * wave + i);
-            const uint32_t oa = opaque_v(vsa) + (so + (uint32_t)(16 * i) * kq);
-            const uint32_t ob = opaque_v(vsb) + (so + (uint32_t)sir * kq);
-            dma4(dAs, oks ? oa : OOB, LSA + ldst);
-            dma4(dBs, oks ? ob : OOB, LSB + ldst);
+            const uint32_t oa = vsa + (so + (uint32_t)(16 * i) * kq);
+            const uint32_t ob = vsb + (so + (uint32_t)sir * kq);
+            dma_lds_r<4>(dAs, oks ? oa : OOB, LSA + ldst);
+            dma_lds_r<4>(dBs, oks ? ob : OOB, LSB + ldst);
         }
     };
     // the tile's row and column scales into buffer rb
@@ -282,11 +285,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
         const uint32_t co = ((f < 4) ? fa : fb) + q * FS_CODE_TILE + (uint32_t)(32 * i * FS_CB);
         const uint32_t so = ((f < 4) ? fsa : fsb) + q * FS_SCALE_TILE + (uint32_t)(32 * i * FS_SB) + 4 * gg;
         r.c[f] = *(const __attribute__((address_space(3))) u32x4*)(lds + co + (fr ^ (32u * gg)));
-        r.s[f] = *(const __attribute__((address_space(3))) uint32_t*)(lds + so);
+        r.s[f] = *(const __attribute__((address_space(3))) uint16_t*)(lds + so);
     };
     // this lane's two block scales of fragment f in the group, as fp16
     auto conv_scale = [&](const FwdRaw& r, int f) -> half2v {
-        return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.s[f] >> (16 * g), 1.0f, false);
+        return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.s[f], 1.0f, false);
     };
 
     // Tile pipeline.  A tile's super-stage 0 lives in ring slot `par`.  The

@@ -99,6 +99,21 @@ __device__ __forceinline__ void dma_lds(i32x4 desc, uint32_t voff, uint32_t lds_
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 1, voff, 0, 0, 0);
 }
 __device__ __forceinline__ void dma16(i32x4 desc, uint32_t voff, uint32_t lds_base) { dma_lds<16>(desc, voff, lds_base); }
+
+// The same DMA from a ready-made buffer resource (a tile's operand kept as a
+// resource is not rebuilt from its descriptor words at every instruction).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <int SIZE>  // 16 or 4
+__device__ __forceinline__ void dma_lds_r(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    __attribute__((address_space(3))) void* dst = (__attribute__((address_space(3))) void*)(uintptr_t)lds_base;
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, voff, 0, 0, 0);
+}
 __device__ __forceinline__ void dma4(i32x4 desc, uint32_t voff, uint32_t lds_base) { dma_lds<4>(desc, voff, lds_base); }
 __device__ __forceinline__ void dma1(i32x4 desc, uint32_t voff, uint32_t lds_base) { dma_lds<1>(desc, voff, lds_base); }
 
