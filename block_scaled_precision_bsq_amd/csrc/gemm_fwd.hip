@@ -77,7 +77,6 @@ constexpr int FS_CB = FS_K / 2;           // code bytes per row per super-stage
 constexpr int FS_SB = FS_K / 16;          // scale bytes per row per super-stage
 constexpr int FS_CODE_TILE = 256 * FS_CB; // one operand's codes (32 KB)
 constexpr int FS_SCALE_TILE = 256 * FS_SB;
-constexpr int FS_DMA = 24;                // DMA instructions per wave per super-stage
 
 struct FwdSmem {
     uint8_t a[2][FS_CODE_TILE];
@@ -125,7 +124,7 @@ __device__ __forceinline__ void dequant_half(half8& out, uint32_t w, _Float16 s)
     out[4 * H + 3] = p1[1];
 }
 
-template <bool OUT_F32, bool SWIGLU>
+template <bool OUT_F32, bool SWIGLU, bool KFULL>
 __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     static_assert(!(OUT_F32 && SWIGLU), "the activation output is bf16");
     extern __shared__ __align__(16) uint8_t smem_raw[];
@@ -158,7 +157,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     const uint32_t dch0 = (uint32_t)((lane & 7) ^ swz8(lane >> 3));
     const uint32_t dch1 = (uint32_t)((lane & 7) ^ swz8(8 + (lane >> 3)));
     // Scale DMA: instruction i (0..3) covers rows 64 * wave + 16i + lane / 4,
-    // dword lane & 3 of the row's 16 scale bytes.
+    // dword lane & 3 of the row's 16 scale bytes.  KFULL (K a multiple of
+    // 256, scale rows 16-byte aligned): one instruction per operand moves
+    // row 64 * wave + lane's 16 bytes.
     const int srow0 = 64 * wave + (lane >> 2);
     const uint32_t sdw = (uint32_t)(lane & 3);
     // Fragment reads: lane (lr, g) of group gg takes logical chunk 2gg + g of
@@ -201,6 +202,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
     const uint32_t vrb = (uint32_t)((SWIGLU ? 2 : 4) * (lane >> 3)) * KB;
     const uint32_t vsa = (uint32_t)srow0 * KS + 4 * sdw;
     const uint32_t vsb = (uint32_t)((SWIGLU ? 2 : 4) * (lane >> 2)) * KS + 4 * sdw;
+    const uint32_t vsa16 = (uint32_t)(64 * wave + lane) * KS;
+    const uint32_t vsb16 = (uint32_t)((SWIGLU ? 2 : 4) * (lane & 31) + (lane >> 5)) * KS;
     const uint32_t vch0 = 16 * dch0, vch1 = 16 * dch1;
     // with the chunk of each parity folded in (instruction i uses parity i & 1)
     const uint32_t va0 = vra + vch0, va1 = vra + vch1, vb0 = vrb + vch0, vb1 = vrb + vch1;
@@ -248,12 +251,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
             const int bir = SWIGLU ? 16 * (i & 3) + (i >> 2) : 32 * (i & 3) + (i >> 2);
             const uint32_t kb = opaque_s(KB);
             const uint32_t ks = (uint32_t)S * FS_CB;
-            const bool okk = ok & (ks + ((i & 1) ? vch1 : vch0) < KB);  // chunk inside the row (K tail)
+            // chunk inside the row (only the last super-stage of a K tail has any outside)
+            const bool okk = KFULL ? ok : ok & (ks + ((i & 1) ? vch1 : vch0) < KB);
             const uint32_t ldst = q * FS_CODE_TILE + 1024u * (uint32_t)(8 * wave + i);
             const uint32_t oa = ((i & 1) ? va1 : va0) + (ks + (uint32_t)(8 * i) * kb);
             const uint32_t ob = ((i & 1) ? vb1 : vb0) + (ks + (uint32_t)bir * kb);
             dma_lds_r<16>(dA, okk ? oa : OOB, LA + ldst);
             dma_lds_r<16>(dB, okk ? ob : OOB, LB + ldst);
+        } else if constexpr (KFULL) {
+            // B: ring position 64 w + lane holds local row bw0 + 4 (lane % 32) + lane / 32
+            // (SWIGLU: 2 (lane % 32))
+            if (part == 8) {
+                const uint32_t so = (uint32_t)S * FS_SB;
+                const uint32_t ldst = q * FS_SCALE_TILE + 1024u * (uint32_t)wave;
+                dma_lds_r<16>(dAs, ok ? vsa16 + so : OOB, LSA + ldst);
+                dma_lds_r<16>(dBs, ok ? vsb16 + so : OOB, LSB + ldst);
+            }
         } else {
             const int i = part - 8;
             // B: ring position 64 w + 16 i + lane / 4 holds local row bw0 + 4 (lane / 4) + sir
@@ -527,9 +540,12 @@ hipError_t launch_gemm_fwd_nvfp4v(const uint8_t* a_codes, const uint8_t* a_bscal
     if (err != hipSuccess) return err;
     static bool attr_set = false;  // idempotent; racing writers set the same value
     if (!attr_set) {
-        const void* ks[3] = {reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<true, false>),
-                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false, false>),
-                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false, true>)};
+        const void* ks[6] = {reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<true, false, false>),
+                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false, false, false>),
+                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false, true, false>),
+                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<true, false, true>),
+                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false, false, true>),
+                             reinterpret_cast<const void*>(&k_gemm_fwd_nvfp4v<false, true, true>)};
         for (const void* k : ks) {
             err = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                       (int)(sizeof(FwdSmem) + lds_table_bytes(LDS_TABLE_MAX_E)));
@@ -539,12 +555,19 @@ hipError_t launch_gemm_fwd_nvfp4v(const uint8_t* a_codes, const uint8_t* a_bscal
     }
     FwdArgs p{a_codes, a_bscale, a_rscale, w_codes, w_bscale, w_rscale, offsets, E, N, K, y, y_f32, plan, ldo};
     const size_t lds = sizeof(FwdSmem) + lds_table_bytes(E);
-    if (swiglu)
-        hipLaunchKernelGGL((k_gemm_fwd_nvfp4v<false, true>), dim3(grid), dim3(256), lds, s, p);
-    else if (y_f32)
-        hipLaunchKernelGGL((k_gemm_fwd_nvfp4v<true, false>), dim3(grid), dim3(256), lds, s, p);
-    else
-        hipLaunchKernelGGL((k_gemm_fwd_nvfp4v<false, false>), dim3(grid), dim3(256), lds, s, p);
+    // whole 256-element super-stages and 16-byte aligned scale rows: each
+    // row's 16 scale bytes of a super-stage move as one 16-byte load
+    const bool kfull = K % FS_K == 0 && (reinterpret_cast<uintptr_t>(a_bscale) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(w_bscale) & 15) == 0;
+#define BSQ_FWD_LAUNCH(F32, SW, KF) hipLaunchKernelGGL((k_gemm_fwd_nvfp4v<F32, SW, KF>), dim3(grid), dim3(256), lds, s, p)
+    if (swiglu) {
+        if (kfull) BSQ_FWD_LAUNCH(false, true, true); else BSQ_FWD_LAUNCH(false, true, false);
+    } else if (y_f32) {
+        if (kfull) BSQ_FWD_LAUNCH(true, false, true); else BSQ_FWD_LAUNCH(true, false, false);
+    } else {
+        if (kfull) BSQ_FWD_LAUNCH(false, false, true); else BSQ_FWD_LAUNCH(false, false, false);
+    }
+#undef BSQ_FWD_LAUNCH
     return hipGetLastError();
 }
 
