@@ -401,8 +401,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd_nvfp4v(FwdArgs p) {
                         if (j == 0 && k < 8) read_part(G + 1, nxt, k);
                         // refill of the slot just freed with super-stage S+2
                         // (this tile's super-stage S+2, else the next tile's S+2-nsup)
-                        if (gg == 3 && j == 1 && k < 12)
-                            issue_part(S + 2 < nsup ? S + 2 : S + 2 - nsup, ((uint32_t)S + par) & 1, k,
+                        // (6 parts in each of k steps 1 and 2: a burst of DMA
+                        // instructions stalls the wave issuing them)
+                        if (gg == 3 && (j == 1 || j == 2) && k < 6)
+                            issue_part(S + 2 < nsup ? S + 2 : S + 2 - nsup, ((uint32_t)S + par) & 1, 6 * (j - 1) + k,
                                        (S + 2 < nsup) | has_next);
                         __builtin_amdgcn_sched_barrier(0);
                     }
