@@ -106,9 +106,44 @@ def _fwd_case(orc, bsq, counts, n, k, seed):
     ([1000], 512, 1024),                        # one expert = dense GEMM
     ([40, 70, 9], 264, 64),                     # n not a tile multiple, k = one chunk
     ([129, 255, 257], 128, 448),                # k % 128 == 64 tail stage
+    ([129, 300, 0, 41], 256, 768),              # three 256-element super-stages: the shortest tile
+                                                # whose refill fetches the next tile's operands
+    ([300, 77], 264, 640),                      # three super-stages, the last one partial
 ])
 def test_fwd_parity(orc, bsq_gpu, counts, n, k):
     _fwd_case(orc, bsq_gpu, counts, n, k, seed=n + k)
+
+
+def test_fwd_scale_rows_not_16_byte_aligned(orc, bsq_gpu):
+    """The forward GEMM moves a row's 16 scale bytes per super-stage as one
+    16-byte load only when k is a multiple of 256 and both block-scale
+    buffers are 16-byte aligned; scale buffers 4 bytes past a 16-byte
+    boundary take the dword path and must give the same bits."""
+    counts, n, k = [300, 0, 129, 40], 256, 1024
+    rng = rng_for(3, salt=4321)
+    off = offsets_from_counts(counts)
+    M, E = int(off[-1]), len(counts)
+    x = make_quantize_input(rng, M, k)
+    w = normal_bf16(rng, (E * n, k), 0.02)
+    a_d = bsq_gpu.bsq_quantize_nvfp4v(_bf16_dev(x))
+    w_d = bsq_gpu.bsq_quantize_nvfp4v(_bf16_dev(w))
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 16, dtype=torch.uint8, device=t.device)
+        base = (16 - buf.data_ptr() % 16) % 16 + 4
+        v = buf[base:base + t.numel()].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 == 4
+        return v
+
+    offd = _to_dev(off)
+    y_al = _np(bsq_gpu.bsq_grouped_gemm_fwd(a_d, w_d, offd, n, k, y_dtype=bsq_gpu.BSQ_F32))
+    a_s = (a_d[0], shifted(a_d[1]), a_d[2])
+    w_s = (w_d[0], shifted(w_d[1]), w_d[2])
+    y_un = _np(bsq_gpu.bsq_grouped_gemm_fwd(a_s, w_s, offd, n, k, y_dtype=bsq_gpu.BSQ_F32))
+    assert np.array_equal(y_al.view(np.uint32), y_un.view(np.uint32))
+    ref = orc.grouped_gemm_fwd(orc.quantize_nvfp4v(x), orc.quantize_nvfp4v(w), off)
+    check_groups(y_un.astype(np.float64), ref, [(f"expert{e}", np.arange(off[e], off[e + 1])) for e in range(E)])
 
 
 def test_fwd_deterministic(orc, bsq_gpu):
@@ -403,16 +438,17 @@ def test_gemm_row_batch_invariance(orc, bsq_gpu):
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
 
-@pytest.mark.parametrize("E", [200, 900])
-def test_many_experts(orc, bsq_gpu, E):
+@pytest.mark.parametrize("E,k", [(200, 128), (900, 128), (900, 768)])
+def test_many_experts(orc, bsq_gpu, E, k):
     """Many small experts, a third of them empty: 200 experts decode through
     several wave-wide rounds of the LDS tables, 900 exceed the LDS tables and
-    decode from the planner's arrays in global memory."""
-    rng = rng_for(7, salt=E)
+    decode from the planner's arrays in global memory (k = 768: while tiles
+    fetch the next tile's operands ahead)."""
+    rng = rng_for(7, salt=E + k)
     counts = rng.integers(0, 24, E)
     counts[rng.random(E) < 0.33] = 0
-    _fwd_case(orc, bsq_gpu, list(counts), 64, 128, seed=E)
-    _bwd_case(orc, bsq_gpu, list(counts), 64, 128, seed=E + 1)
+    _fwd_case(orc, bsq_gpu, list(counts), 64, k, seed=E + k)
+    _bwd_case(orc, bsq_gpu, list(counts), 64, k, seed=E + k + 1)
 
 
 def test_invalid_offsets_reported(bsq_gpu):

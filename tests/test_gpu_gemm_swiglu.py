@@ -50,6 +50,7 @@ def _h_vs_oracle(orc, h_bits, gu_gpu_bits, gu_ref_bits, inter):
     ([300, 0, 17, 1, 256, 513], 128, 256),      # ragged, empty, one-token experts, several row tiles
     ([129, 255, 257], 256, 448),                # two column tiles, k % 128 == 64 tail stage
     ([1000], 384, 1024),                        # one expert, three column tiles
+    ([513, 2, 260], 128, 768),                  # three super-stages: the next tile fetched ahead
 ])
 def test_gemm_swiglu_parity(orc, bsq_gpu, counts, inter, k):
     rng = rng_for(3, salt=inter + k)
