@@ -202,8 +202,19 @@ struct MxBlock {
     uint32_t sbyte; // E8M0
 };
 
-// Encode one block of 32 floats given as 16 bf16 pairs.
+// Encode one block of 32 values given as 16 bf16 pairs.  Each pair goes
+// through v_cvt_scalef32_pk_fp8_bf16, which divides by a power-of-two scale
+// and rounds to E4M3 (nearest even) -- exact, since the scale is a power of
+// two -- but turns results past 448 into NaN instead of saturating, so the
+// bf16 magnitudes are first clamped to 448 * 2^sh on their bit patterns
+// (one unsigned and one signed packed 16-bit min: bf16 is sign-magnitude).
+// The instruction's behaviour (byte order, word select, every bf16 pattern
+// at scales 2^-127 .. 2^127) was checked against the definition on the GPU.
 __device__ __forceinline__ MxBlock mx_encode(const uint32_t (&w)[16]) {
+    typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+    typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
     uint32_t m = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) m = absmax2_bf16(m, w[j]);
@@ -221,14 +232,25 @@ __device__ __forceinline__ MxBlock mx_encode(const uint32_t (&w)[16]) {
     const int e = biased ? biased - 127 : -127;
     const int sh = min(max(e - 8, -127), 127);
     r.sbyte = (uint32_t)(sh + 127);
+    // 448 * 2^sh as bf16 bits (finite inputs give sh <= 119), and 2^sh as the
+    // fp32 scale (2^-127 is subnormal)
+    const uint32_t T = ((uint32_t)(sh + 135) << 7) | 0x60u;
+    const u16x2 tu = {(uint16_t)(T | 0x8000u), (uint16_t)(T | 0x8000u)};
+    const i16x2 ti = {(int16_t)T, (int16_t)T};
+    const float scale = __uint_as_float(sh > -127 ? (uint32_t)(sh + 127) << 23 : 0x00400000u);
+    auto clamp2 = [&](uint32_t x) -> bf16x2 {
+        // negative values keep their sign bit through the unsigned min and are
+        // below T as signed; positive ones pass the unsigned min unchanged
+        const u16x2 a = __builtin_elementwise_min(__builtin_bit_cast(u16x2, x), tu);
+        return __builtin_bit_cast(bf16x2, __builtin_elementwise_min(__builtin_bit_cast(i16x2, a), ti));
+    };
     uint32_t out[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        // x * 2^-sh is exact except for results far below E4M3's smallest
-        // subnormal, which encode to (signed) zero either way.
-        out[j] = e4m3x4(__builtin_ldexpf(bf16_lo(w[2 * j]), -sh), __builtin_ldexpf(bf16_hi(w[2 * j]), -sh),
-                        __builtin_ldexpf(bf16_lo(w[2 * j + 1]), -sh),
-                        __builtin_ldexpf(bf16_hi(w[2 * j + 1]), -sh));
+        s16x2 o = {0, 0};
+        o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, clamp2(w[2 * j]), scale, false);
+        o = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, clamp2(w[2 * j + 1]), scale, true);
+        out[j] = __builtin_bit_cast(uint32_t, o);
     }
     r.c0 = make_uint4(out[0], out[1], out[2], out[3]);
     r.c1 = make_uint4(out[4], out[5], out[6], out[7]);
