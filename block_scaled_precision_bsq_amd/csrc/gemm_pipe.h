@@ -2,19 +2,18 @@
 //
 // Operand tiles travel global -> LDS through the buffer-load-to-LDS path
 // ("buffer_load_dwordx4 ... lds"): each wave instruction writes 64 lanes x 16
-// bytes to 1 KB of consecutive LDS starting at M0, with no VGPR staging.  A
-// stage holds 256 rows x 64 bytes per operand; 16 rows fill one instruction,
-// so rows are stored unpadded and the 16-byte chunks of row r are permuted by
-// an XOR swizzle, chunk c living at slot c ^ swz(r).  swz(r) =
-// ((r >> 1) ^ (r >> 2)) & 3 makes the fragment reads -- 16 consecutive rows,
-// one chunk each -- hit 16 distinct 4-bank groups (and 8 rows, 8 groups).
+// bytes to 1 KB of consecutive LDS starting at M0, with no VGPR staging.
+// Rows are stored unpadded; the 16-byte chunks of a row are permuted by an
+// XOR swizzle (swz8 below) so that fragment reads, which take one chunk from
+// each of 16 or 32 consecutive rows, spread over all banks.  Each kernel
+// describes its own ring of stages.
 //
-// Four stages form a ring.  The loads are issued from inline assembly, so the
-// compiler does not see LDS writes in flight and inserts no waits for them;
-// the kernel waits explicitly: s_waitcnt vmcnt(N) for its own DMA groups (the
-// counter retires in order), then s_barrier so every wave's part of a stage is
-// in LDS before anyone reads it, and s_waitcnt lgkmcnt(0) before the barrier
-// that precedes overwriting a ring slot, so all reads of that slot are done.
+// The loads go through the compiler's LDS-DMA builtin.  The kernels wait for
+// them explicitly: s_waitcnt vmcnt(N) for their own DMA groups (the counter
+// retires vector-memory operations in issue order on this target), then
+// s_barrier so every wave's part of a stage is in LDS before anyone reads
+// it, and s_waitcnt lgkmcnt(0) before the barrier that precedes overwriting a
+// ring slot, so all reads of that slot are done.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,21 +29,13 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-constexpr int PIPE_ROWS = 256;                  // rows per operand tile
-constexpr int PIPE_BK = 64;                     // bytes per row per stage
-constexpr int PIPE_STAGE_BYTES = PIPE_ROWS * PIPE_BK;
-constexpr int PIPE_NST = 4;                     // ring depth
-
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+constexpr int PIPE_ROWS = 256;  // rows per operand tile
 
 // 128-byte rows hold 8 chunks of 16 bytes; chunk c of row r lives in slot
 // c ^ swz8(r).  A 16-lane quarter of a fragment read covers 16 consecutive
 // rows at one chunk: rows of equal parity share 8-chunk halves of the 64 LDS
 // banks and swz8 = (r >> 1) & 7 spreads them over all 8 slots.
 __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
-
-// Byte offset of logical 16-byte chunk c of row r inside a stage buffer.
-__device__ __forceinline__ int swz_off(int r, int c) { return r * PIPE_BK + 16 * (c ^ swz(r)); }
 
 // Raw buffer descriptor (base, stride 0, num_records, gfx9 data format).
 __device__ __forceinline__ i32x4 make_desc(const void* base) {
@@ -54,14 +45,6 @@ __device__ __forceinline__ i32x4 make_desc(const void* base) {
     r.y = (int)((a >> 32) & 0xFFFFu);
     r.z = 0x7FFFFFFF;
     r.w = 0x00020000;
-    return r;
-}
-
-// Descriptor whose byte range ends at `bytes`: offsets at or past it read as
-// zero (the row limit of a partial tile).
-__device__ __forceinline__ i32x4 make_desc_n(const void* base, uint32_t bytes) {
-    i32x4 r = make_desc(base);
-    r.z = (int)bytes;
     return r;
 }
 
