@@ -109,6 +109,9 @@ def _fwd_case(orc, bsq, counts, n, k, seed):
     ([129, 300, 0, 41], 256, 768),              # three 256-element super-stages: the shortest tile
                                                 # whose refill fetches the next tile's operands
     ([300, 77], 264, 640),                      # three super-stages, the last one partial
+    ([128, 384, 129, 385, 64], 264, 768),       # expert tails of 128, 128, 129, 129, 64 rows: the
+                                                # half-height loop (<= 128 rows) and its boundary
+    ([128, 64, 200], 256, 256),                 # half-height tiles with one super-stage
 ])
 def test_fwd_parity(orc, bsq_gpu, counts, n, k):
     _fwd_case(orc, bsq_gpu, counts, n, k, seed=n + k)

@@ -51,6 +51,7 @@ def _h_vs_oracle(orc, h_bits, gu_gpu_bits, gu_ref_bits, inter):
     ([129, 255, 257], 256, 448),                # two column tiles, k % 128 == 64 tail stage
     ([1000], 384, 1024),                        # one expert, three column tiles
     ([513, 2, 260], 128, 768),                  # three super-stages: the next tile fetched ahead
+    ([128, 384, 129, 1], 128, 768),             # tails of 128 and 1 rows (half-height loop), 129 (full)
 ])
 def test_gemm_swiglu_parity(orc, bsq_gpu, counts, inter, k):
     rng = rng_for(3, salt=inter + k)
