@@ -41,10 +41,10 @@
 // bytes), with no LDS staging and no barrier.
 //
 // Schedule: each k step issues its 16 MFMAs with the dequantization of the
-// next step (8 fragments, half a fragment per MFMA), the LDS reads of the
-// next group and, once per super-stage, the ring refill pinned between them
-// by sched_barrier, so VALU, LDS and DMA work runs in the matrix core's
-// shadow.  The loop body has no branches: a branch splits the schedule into
+// next step (8 fragments, half a fragment per MFMA; half-height tiles: 8
+// MFMAs, 6 fragments), the LDS reads of the next group and, once per
+// super-stage, the ring refill pinned between them by sched_barrier, so
+// VALU, LDS and DMA work runs in the matrix core's shadow.  The loop body has no branches: a branch splits the schedule into
 // blocks, and the compiler then sinks each step's dequantization past it,
 // next to the MFMAs that wait for it.
 //
