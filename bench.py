@@ -541,17 +541,21 @@ def frozen_w4a16(bsq, torch, dev, x, h, q_wgu, q_wdn, off, E, Hd, I, M, bf16_bas
 
 
 def kernel_source_hash(stage):
-    """Hash of the sources a stage's kernel is built from (kernel file plus the
-    shared headers), used to tell whether stored counter readings still
-    describe the kernel as it is now."""
+    """Hash of the code a stage's kernel is built from (kernel file plus the
+    shared headers, comments and blank space removed), used to tell whether
+    stored counter readings still describe the kernel as it is now."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "block_scaled_precision_bsq_amd", "csrc")
     main = ("gemm_fwd.hip" if stage.startswith("gemm_fwd") else "gemm_bwd.hip" if stage.startswith("gemm_bwd")
             else "quantize.hip")
     h = hashlib.sha256()
     for f in (main, "device_common.h", "gemm_common.h", "gemm_pipe.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)   # block comments
+        code = re.sub(r"//[^\n]*", " ", code)                 # line comments
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
